@@ -1,0 +1,120 @@
+"""fp64 CPU oracle for C = relu(A·B): TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The gfx950 library never calls it and
+shares no code with it; this package does not import the library either.
+
+The arithmetic lives in ``mmrelu_oracle.c`` (plain C, OpenMP over rows),
+built with gcc into ``liboracle.so`` next to it. Each routine is the plain
+definition R[i][j] = max(0, sum_k A[i][k]·B[k][j]) in fp64 with ascending k;
+see the C file for the passages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "mmrelu_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (no fast-math: IEEE double semantics)."""
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    lib = ctypes.CDLL(LIB)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("oracle_mmrelu_f32", "oracle_mmrelu_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_mmrelu_f32_at", "oracle_mmrelu_bf16_at"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
+        fn.restype = None
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def _check(a: np.ndarray, b: np.ndarray, M, N, K, lda, ldb, dtype):
+    if a.dtype != dtype or b.dtype != dtype:
+        raise TypeError(f"oracle inputs must be {dtype}")
+    if not (a.flags.c_contiguous and b.flags.c_contiguous):
+        raise ValueError("oracle inputs must be C-contiguous buffers")
+    if min(M, N, K) < 0 or lda < max(1, K) or ldb < max(1, N):
+        raise ValueError("bad sizes or leading dimensions")
+    if M > 0 and K > 0 and a.size < (M - 1) * lda + K:
+        raise ValueError("A buffer too small")
+    if K > 0 and N > 0 and b.size < (K - 1) * ldb + N:
+        raise ValueError("B buffer too small")
+
+
+def _dtype_and_fns(a: np.ndarray):
+    if a.dtype == np.float32:
+        return np.float32, "oracle_mmrelu_f32", "oracle_mmrelu_f32_at"
+    if a.dtype == np.uint16:
+        return np.uint16, "oracle_mmrelu_bf16", "oracle_mmrelu_bf16_at"
+    raise TypeError("oracle inputs are float32 or uint16 (bf16 bit patterns)")
+
+
+def mmrelu(a: np.ndarray, b: np.ndarray, M=None, N=None, K=None, lda=None, ldb=None) -> np.ndarray:
+    """relu(A·B) as an M x N float64 array. ``a``/``b`` are float32 (fp32) or
+    uint16 (bf16 bit patterns) row-major buffers with leading dimensions lda/ldb
+    (defaults: the arrays' 2-D shapes)."""
+    dtype, full, _ = _dtype_and_fns(a)
+    if M is None:
+        M, lda = a.shape[0], a.shape[1]
+        K = K if K is not None else a.shape[1]
+        ldb = b.shape[1]
+        N = N if N is not None else b.shape[1]
+    lda = lda if lda is not None else K
+    ldb = ldb if ldb is not None else N
+    _check(a, b, M, N, K, lda, ldb, dtype)
+    r = np.empty((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return r
+    rc = getattr(_load(), full)(a.ctypes.data, b.ctypes.data, r.ctypes.data, M, N, K, lda, ldb, N)
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its row accumulator")
+    return r
+
+
+def mmrelu_at(a: np.ndarray, b: np.ndarray, rows, cols, K: int, lda: int, ldb: int) -> np.ndarray:
+    """relu(A·B)[rows[t], cols[t]] for each t, as float64 (one dot product each)."""
+    dtype, _, at = _dtype_and_fns(a)
+    ii = np.ascontiguousarray(rows, dtype=np.int64)
+    jj = np.ascontiguousarray(cols, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("rows and cols differ in length")
+    if ii.size and (ii.min() < 0 or jj.min() < 0):
+        raise ValueError("negative index")
+    if ii.size and K > 0:
+        if a.size < ii.max() * lda + K or b.size < (K - 1) * ldb + jj.max() + 1:
+            raise ValueError("index beyond the buffers")
+    out = np.empty(ii.size, dtype=np.float64)
+    if ii.size:
+        getattr(_load(), at)(a.ctypes.data, b.ctypes.data, K, lda, ldb,
+                             ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
+    return out

@@ -1,0 +1,148 @@
+/*
+ * Oracle for C = relu(A·B): TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library. It shares no code with the gfx950 library: no
+ * headers, helpers, tables or pre/post-processing.
+ *
+ * What it computes (lecture notes "Kernels, Triton, XLA", section
+ * "Reductions and tiling", matmul finale; and the Chinese notes' section 5.5
+ * on matrix multiplication, the matmul_relu_kernel listing): A is M x K, B is
+ * K x N, C is M x N, and every output element is the K-term dot product of a
+ * row of A with a column of B, passed through ReLU (max with 0) before it is
+ * stored. Tiling only changes the order in which the same products are
+ * summed, so the oracle is the plain definition:
+ *
+ *     s      = sum over k = 0 .. K-1, in ascending k, of A[i][k] * B[k][j]
+ *     R[i][j] = s > 0 ? s : 0
+ *
+ * evaluated in IEEE double precision. Inputs are fp32 (or bf16 widened to
+ * fp32 by placing the 16 stored bits in the high half of a 32-bit word), and
+ * every fp32 x fp32 product is exact in double (24 + 24 <= 53 significand
+ * bits), so only the K-1 additions round. The result stays in double.
+ *
+ * Matrices are row-major with leading dimensions in elements:
+ * A[i][k] = A[i*lda + k], B[k][j] = B[k*ldb + j], R[i][j] = R[i*ldr + j].
+ *
+ * The full-matrix routines loop i, then k, then j with one double
+ * accumulator per output column. Each R[i][j] is still a single running sum
+ * taken in ascending k, so the result is bit-identical to the i, j, k order
+ * and does not depend on the number of threads (rows are split over OpenMP
+ * threads; a row is never split). The "_at" routines evaluate single entries
+ * with the i, j, k order directly, for sampled checks at large sizes.
+ *
+ * The sign of a zero result and NaN inputs are outside what the pages fix:
+ * s <= 0 (including -0.0) gives +0.0, and a NaN sum gives 0 (parity
+ * unpinned for NaN and infinities; the workloads never produce them).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double relu(double s) { return s > 0.0 ? s : 0.0; }
+
+static double widen_bf16(uint16_t h)
+{
+    uint32_t w = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full relu(A·B) for fp32 inputs into a double M x N matrix R (ld ldr).
+ * Returns 0, or -1 if a row accumulator could not be allocated. */
+int oracle_mmrelu_f32(const float *A, const float *B, double *R,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldr)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            if (!acc) continue;
+            for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = (double)A[i * lda + k];
+                const float *brow = B + k * ldb;
+                for (int64_t j = 0; j < N; ++j) acc[j] += a * (double)brow[j];
+            }
+            for (int64_t j = 0; j < N; ++j) R[i * ldr + j] = relu(acc[j]);
+        }
+        free(acc);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Same for bf16 inputs given as uint16 bit patterns. */
+int oracle_mmrelu_bf16(const uint16_t *A, const uint16_t *B, double *R,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldr)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            if (!acc) continue;
+            for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double a = widen_bf16(A[i * lda + k]);
+                const uint16_t *brow = B + k * ldb;
+                for (int64_t j = 0; j < N; ++j) acc[j] += a * widen_bf16(brow[j]);
+            }
+            for (int64_t j = 0; j < N; ++j) R[i * ldr + j] = relu(acc[j]);
+        }
+        free(acc);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Entries R[ii[t]][jj[t]] for t < n, each as one dot product in ascending k. */
+void oracle_mmrelu_f32_at(const float *A, const float *B, int64_t K,
+                          int64_t lda, int64_t ldb,
+                          const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (double)A[ii[t] * lda + k] * (double)B[k * ldb + jj[t]];
+        out[t] = relu(s);
+    }
+}
+
+void oracle_mmrelu_bf16_at(const uint16_t *A, const uint16_t *B, int64_t K,
+                           int64_t lda, int64_t ldb,
+                           const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += widen_bf16(A[ii[t] * lda + k]) * widen_bf16(B[k * ldb + jj[t]]);
+        out[t] = relu(s);
+    }
+}
