@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of C = relu(A·B) on one MI355X through the gfx950 C-ABI library.
+
+A step is one call of the library on the headline workload: bf16 inputs and
+output, fp32 accumulation, M = N = K = 8192, entries N(0,1)/sqrt(K) rounded
+to bf16, seeded synthetic data already resident in HBM. The fp32 4096^3
+U(-1,1) workload is timed the same way and reported beside it.
+
+Prints one JSON line: throughput (TFLOP/s, 2MNK per step), the roofline
+object for the dominant kernel (achieved FLOP/s per launch from HIP events on
+the launch stream against the bf16 dense matrix-core peak) and the CPU
+baseline (the fp64 oracle timed on a bounded sample of the same workload on
+this host's cores).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix-core peaks
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "bf16": ["tiled_matmul_relu_amd/csrc/k_bf16_mfma.hip", "tiled_matmul_relu_amd/csrc/device_common.hpp"],
+    "f32": ["tiled_matmul_relu_amd/csrc/k_f32_mfma.hip", "tiled_matmul_relu_amd/csrc/device_common.hpp"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str, kernel_name: str):
+    """HBM bytes per launch from committed counter runs, or None when the
+    kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_hash(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_device(x, torch):
+    import numpy as np
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def time_workload(cfg, steps, warmup, torch, mm, datagen):
+    a, b = datagen.make_inputs(cfg)
+    da, db = to_device(a, torch), to_device(b, torch)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    c = torch.empty((cfg.M, cfg.ldc), dtype=dt, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = mm.mmrelu_f32 if cfg.dtype == "f32" else mm.mmrelu_bf16
+    args = (da.data_ptr(), db.data_ptr(), c.data_ptr(), cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc,
+            stream.cuda_stream)
+    for _ in range(warmup):
+        rc = fn(*args)
+        if rc != mm.MMRELU_OK:
+            raise RuntimeError(mm.status_string(rc))
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn(*args)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    plan = mm.mmrelu_plan(mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16, cfg.M, cfg.N, cfg.K,
+                          cfg.lda, cfg.ldb, cfg.ldc)
+    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b)}
+
+
+def cpu_baseline(cfg, a, b, target_s, oracle):
+    """The oracle timed on rows [0, r) of the workload, r chosen from a short
+    calibration run so that the timed part takes about target_s seconds."""
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.mmrelu(a, b, M=rows, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
+        return time.perf_counter() - t0
+    cal_rows = 8
+    t_cal = run(cal_rows)
+    rows = int(min(cfg.M, max(cal_rows, target_s / max(t_cal, 1e-6) * cal_rows)))
+    t = run(rows)
+    flops = 2.0 * rows * cfg.N * cfg.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of {cfg.M} of the {cfg.name} workload ({rows}x{cfg.N} outputs, "
+                      f"K={cfg.K}), fp64 oracle, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
+    ap.add_argument("--no-f32", action="store_true", help="skip the fp32 4096^3 workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; relu(A·B) shards by rows or columns of C with no "
+              "exchange, and no multi-GPU path is built. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    import tiled_matmul_relu_amd as mm
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mm.load_library()
+
+    head = datagen.CONFIGS[5]
+    res = time_workload(head, args.steps, args.warmup, torch, mm, datagen)
+    kernel = res["plan"]["name"]
+    achieved = res["tflops"]
+    traffic = measured_traffic("bf16", kernel)
+    out = {
+        "metric": "TFLOP/s and % of MI355X MFMA peak for relu(A·B), fp32 4096³ and bf16 8192³",
+        "value": round(achieved, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(K) rounded to bf16, resident in HBM)",
+        "config": {"workload": "relu(A·B) bf16 in/out, fp32 accumulate, M=N=K=8192, row-major",
+                   "M": head.M, "N": head.N, "K": head.K, "lda": head.lda, "ldb": head.ldb, "ldc": head.ldc,
+                   "kernel": kernel, "grid": res["plan"]["grid"]},
+        "pct_of_peak": round(100 * achieved / PEAK_TFLOPS["bf16"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic},
+    }
+    if not args.no_f32:
+        f = datagen.CONFIGS[3]
+        r32 = time_workload(f, args.steps, args.warmup, torch, mm, datagen)
+        out["fp32_4096"] = {"value": round(r32["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r32["ms"], 4),
+                            "frac": round(r32["tflops"] / PEAK_TFLOPS["f32"], 4), "peak": PEAK_TFLOPS["f32"],
+                            "kernel": r32["plan"]["name"],
+                            "traffic": measured_traffic("f32", r32["plan"]["name"])}
+    if not args.no_cpu_baseline:
+        import oracle
+        a, b = res["inputs"]
+        out["cpu_baseline"] = cpu_baseline(head, a, b, args.cpu_seconds, oracle)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

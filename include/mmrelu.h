@@ -1,0 +1,130 @@
+/*
+ * mmrelu: C = relu(A·B) on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the lecture's matmul finale with the fused activation
+ * ("Kernels, Triton, XLA" lecture notes, section "Reductions and tiling",
+ * the matmul paragraph and its kernel sketch; the Chinese notes' section 5.5,
+ * listing matmul_relu_kernel): A is M x K, B is K x N, C is M x N, each output
+ * tile accumulates its K-term dot products in fp32, applies max(x, 0), and is
+ * stored once, with loads and the store masked at the matrix edges.
+ *
+ * Layout: every matrix is row-major with a leading dimension in ELEMENTS:
+ *     A[i][k] = A[i*lda + k],  B[k][j] = B[k*ldb + j],  C[i][j] = C[i*ldc + j]
+ * and for 0 <= i < M, 0 <= j < N:
+ *     C[i][j] = max(0, sum_{k<K} A[i][k] * B[k][j])
+ * (the lecture's kernel takes a stride per dimension; this interface fixes the
+ * column strides to 1, the row-major case).
+ *
+ * Ownership and execution: all pointers are DEVICE pointers owned by the
+ * caller; the library never allocates, frees, or synchronises. The caller
+ * allocates C (as on the pages, where the host allocates the output and the
+ * kernel writes into it). Work is enqueued on `stream` (a hipStream_t; NULL
+ * means the null stream) and the call returns right after the enqueue, so a
+ * device-side fault is reported by the caller's next synchronisation. Calls
+ * are thread-safe and reentrant (the library keeps no mutable state beyond a
+ * per-device cache of the compute-unit count). Elements of C outside the
+ * M x N window (row padding between N and ldc) are never written. C must not
+ * overlap A or B (not checked).
+ *
+ * Errors: arguments are checked BEFORE anything is enqueued; on any non-zero
+ * status nothing has been launched and C is untouched.
+ *   MMRELU_ERR_INVALID_VALUE  M, N or K negative; lda < max(1,K), ldb < max(1,N),
+ *                             ldc < max(1,N); or a size past the limits below.
+ *   MMRELU_ERR_NULL_POINTER   C null (M, N > 0), or A/B null (M, N, K > 0).
+ *   MMRELU_ERR_MISALIGNED     a pointer not aligned to its element size.
+ *   MMRELU_ERR_LAUNCH         the HIP launch itself failed (hipGetLastError);
+ *                             e.g. the current device is not a gfx950.
+ * Empty outputs (M == 0 or N == 0) return MMRELU_OK without a launch; K == 0
+ * writes C = 0 (the K loop runs zero times and relu(0) is stored).
+ *
+ * Limits: M, N, K <= 2^31 - 1 and lda, ldb, ldc <= 2^21 elements (the kernels
+ * address each tile with 32-bit offsets from a 64-bit tile base).
+ */
+#ifndef MMRELU_H
+#define MMRELU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MMRELU_OK = 0,
+    MMRELU_ERR_INVALID_VALUE = 1,
+    MMRELU_ERR_NULL_POINTER = 2,
+    MMRELU_ERR_MISALIGNED = 3,
+    MMRELU_ERR_LAUNCH = 4
+};
+
+enum { MMRELU_DTYPE_F32 = 0, MMRELU_DTYPE_BF16 = 1 };
+
+/* fp32 inputs, fp32 products accumulated in fp32 on the matrix cores, fp32 output. */
+int mmrelu_f32(const float *A, const float *B, float *C,
+               int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
+/* bf16 inputs and output, given as uint16_t bit patterns; bf16 products
+ * accumulated in fp32; ReLU on the fp32 sum, then rounded to bf16 (nearest,
+ * ties to even). */
+int mmrelu_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
+                int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
+/* Static text for a status code ("unknown status" for anything else). */
+const char *mmrelu_status_string(int status);
+
+/* Library version string. */
+const char *mmrelu_version(void);
+
+/*
+ * Host-only planning (no GPU needed): which kernel variant and grid a call
+ * of this shape would use, and how its workgroups quantise into waves over
+ * the compute units (the lecture's "wave quantization": a last, partial wave
+ * leaves compute units idle).
+ */
+typedef struct {
+    int32_t variant;          /* index in the library's kernel table */
+    int32_t block_m, block_n, block_k;
+    int32_t threads;          /* per workgroup */
+    int32_t wg_per_cu;        /* workgroups resident per compute unit */
+    int32_t cus;              /* compute units assumed */
+    int32_t reserved;
+    int64_t tiles_m, tiles_n, grid;
+    int64_t waves;            /* ceil(grid / (cus * wg_per_cu)) */
+    int64_t idle_slots_last;  /* workgroup slots left empty in the last wave */
+    char name[64];            /* kernel name as a profiler shows it */
+} mmrelu_plan_t;
+
+/* Fill *out for a call of this dtype and shape. cus = 0 uses the current
+ * device's compute-unit count when a device is present, else 256. Returns a
+ * status as above (arguments are validated the same way, pointers aside). */
+int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);
+
+/* Number of kernel variants for a dtype, and the plan a given variant would
+ * use for a shape (variant must be valid for that dtype). For tests and
+ * tuning: it lets every variant be checked on every shape. */
+int mmrelu_num_variants(int dtype);
+int mmrelu_plan_variant(int dtype, int32_t variant, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);
+
+/* Wave quantisation of `blocks` workgroups over `slots` concurrent slots:
+ * *waves = ceil(blocks / slots), *idle_last = slots * waves - blocks.
+ * Returns MMRELU_ERR_INVALID_VALUE for blocks < 0, slots < 1 or null outputs. */
+int mmrelu_wave_quantization(int64_t blocks, int64_t slots, int64_t *waves, int64_t *idle_last);
+
+/* As mmrelu_f32 / mmrelu_bf16 but with an explicit kernel variant instead of
+ * the planner's choice (for tests and tuning). Same checks and semantics. */
+int mmrelu_f32_variant(int32_t variant, const float *A, const float *B, float *C,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+int mmrelu_bf16_variant(int32_t variant, const uint16_t *A, const uint16_t *B, uint16_t *C,
+                        int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMRELU_H */

@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+validates arguments before touching the GPU, and plans grids (no kernel is
+launched here)."""
+import json
+import os
+import re
+
+import pytest
+
+import tiled_matmul_relu_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmrelu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmrelu_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mm.load_library()
+    names = declared_functions()
+    assert "mmrelu_f32" in names and "mmrelu_bf16" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mm.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert mm.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert mm.status_string(s) not in ("ok", "unknown status")
+    assert mm.status_string(99) == "unknown status"
+    assert "gfx950" in mm.version()
+
+
+A, B, C = 0x100000, 0x200000, 0x300000     # aligned fake device addresses (never dereferenced)
+
+
+@pytest.mark.parametrize("fn", [mm.mmrelu_f32, mm.mmrelu_bf16])
+def test_argument_validation_before_launch(fn):
+    E = mm
+    # negative sizes
+    assert fn(A, B, C, -1, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, -1, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, 4, -1, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    # leading dimensions too small / too large
+    assert fn(A, B, C, 4, 4, 8, 7, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, 8, 4, 4, 7, 8) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, 8, 4, 4, 8, 7) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, 4, 4, 0, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 4, 4, 4, (1 << 21) + 1, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fn(A, B, C, 1 << 31, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    # null pointers
+    assert fn(A, B, 0, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_NULL_POINTER
+    assert fn(0, B, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_NULL_POINTER
+    assert fn(A, 0, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_NULL_POINTER
+    # misaligned to the element size
+    assert fn(A + 1, B, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_MISALIGNED
+    assert fn(A, B, C + 1, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_MISALIGNED
+    # empty outputs: OK without a launch, even with null pointers
+    assert fn(0, 0, 0, 0, 4, 4, 4, 4, 4) == E.MMRELU_OK
+    assert fn(0, 0, 0, 4, 0, 4, 4, 1, 1) == E.MMRELU_OK
+
+
+def test_fp32_alignment_only_needs_4_bytes_bf16_2_bytes():
+    # misaligned by 2 bytes: fine for bf16 validation (fails only later for
+    # lack of a GPU, so test with an empty output), not for fp32
+    assert mm.mmrelu_f32(A + 2, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_MISALIGNED
+    assert mm.mmrelu_bf16(A + 2, B, C, 4, 0, 4, 4, 1, 1) == mm.MMRELU_OK
+
+
+def test_variant_entry_points_validate():
+    assert mm.mmrelu_f32_variant(-1, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    assert mm.mmrelu_f32_variant(99, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    assert mm.mmrelu_bf16_variant(99, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    # a variant that needs 16-byte rows refuses an odd leading dimension
+    nv = mm.mmrelu_num_variants(mm.DTYPE_F32)
+    needs_align = [v for v in range(nv) if "unaligned" not in mm.mmrelu_plan_variant(0, v, 8, 8, 8, 8, 8, 8)["name"]
+                   and "mfma" in mm.mmrelu_plan_variant(0, v, 8, 8, 8, 8, 8, 8)["name"]]
+    assert needs_align
+    for v in needs_align:
+        assert mm.mmrelu_f32_variant(v, A, B, C, 5, 5, 5, 5, 5, 5) == mm.MMRELU_ERR_INVALID_VALUE
+
+
+def test_wave_quantization_matches_lecture_arithmetic():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "wave_quantization.json")))
+    for case in g["cases"]:
+        assert mm.mmrelu_wave_quantization(case["blocks"], case["slots"]) == (case["waves"], case["idle_last"])
+        if "tile" in case:
+            assert (case["output"] // case["tile"]) ** 2 == case["blocks"]
+    with pytest.raises(mm.MmreluError):
+        mm.mmrelu_wave_quantization(5, 0)
+
+
+def test_plans_for_the_workloads():
+    # 4096^3 fp32: 128x128 tiles, 1024 workgroups, two resident per CU:
+    # exactly two full waves over 256 CUs (no tail)
+    p = mm.mmrelu_plan(mm.DTYPE_F32, 4096, 4096, 4096, 4096, 4096, 4096, cus=256)
+    assert "mfma" in p["name"] and "unaligned" not in p["name"]
+    assert p["grid"] == p["tiles_m"] * p["tiles_n"]
+    assert p["idle_slots_last"] == 0
+    # ragged 4097 x 3001 x 2049: odd leading dimensions need the dword path
+    p = mm.mmrelu_plan(mm.DTYPE_F32, 4097, 3001, 2049, 2049, 3001, 3001, cus=256)
+    assert "unaligned" in p["name"]
+    assert p["tiles_m"] == -(-4097 // p["block_m"]) and p["tiles_n"] == -(-3001 // p["block_n"])
+    # 8192^3 bf16: matrix-core kernel, whole waves
+    p = mm.mmrelu_plan(mm.DTYPE_BF16, 8192, 8192, 8192, 8192, 8192, 8192, cus=256)
+    assert "bf16_mfma" in p["name"] and p["idle_slots_last"] == 0
+    # bf16 with an odd leading dimension falls back to the plain tiled kernel
+    p = mm.mmrelu_plan(mm.DTYPE_BF16, 100, 100, 100, 100, 100, 100, cus=256)
+    assert "simple" in p["name"]
+    with pytest.raises(mm.MmreluError):
+        mm.mmrelu_plan(mm.DTYPE_F32, -1, 4, 4, 4, 4, 4)
+    with pytest.raises(mm.MmreluError):
+        mm.mmrelu_plan(7, 4, 4, 4, 4, 4, 4)
+
+
+def test_every_variant_plans():
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        n = mm.mmrelu_num_variants(dt)
+        assert n >= 2
+        names = set()
+        for v in range(n):
+            p = mm.mmrelu_plan_variant(dt, v, 1000, 1000, 1000, 1000, 1000, 1000, cus=256)
+            assert p["variant"] == v and p["grid"] == p["tiles_m"] * p["tiles_n"] > 0
+            names.add(p["name"])
+        assert len(names) == n
+
+
+def test_python_wrapper_rejects_bad_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        mm.mmrelu(torch.zeros(2, 2), torch.zeros(2, 2, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        mm.mmrelu(torch.zeros(2, 2), torch.zeros(2, 2))   # host tensors

@@ -1,0 +1,268 @@
+"""Parity of the gfx950 library with the fp64 oracle (needs the GPU).
+
+Every test generates seeded inputs on the host (``datagen``), runs the HIP
+path through the C-ABI, and compares with the oracle on the same inputs:
+  * fp32: max |C - R| <= 1e-4 * sqrt(K), and bit-exact on small-integer
+    inputs (every partial sum is an integer below 2^24, so any summation
+    order is exact).
+  * bf16: ||C - R||_F / ||R||_F <= 1e-2, plus an element-wise bound
+    |C - R| <= 2^-8 |R| + 1e-6 (one bf16 rounding is at most 2^-9 relative;
+    the fp32 accumulation error is orders of magnitude below 1e-6 at these
+    magnitudes), and exact equality with round-to-nearest-even of the oracle
+    on small-integer inputs.
+Small shapes span several tiles with ragged tails and are compared element
+by element; the five full-size workloads run in the configuration the
+benchmark times and are compared on sampled rows, columns and entries that
+the oracle evaluates one by one, plus properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import tiled_matmul_relu_amd as mm
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = lambda K: 1e-4 * math.sqrt(max(K, 1))
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bf16_round_ref(r: np.ndarray) -> np.ndarray:
+    """RNE of fp64 values to bf16 via torch on the CPU (values exactly
+    representable in fp32 here, so fp64 -> fp32 is exact)."""
+    return torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def run(a: np.ndarray, b: np.ndarray, M, N, K, lda, ldb, ldc=None, variant=None, guard=0):
+    """Launch on device copies of a/b; C gets `guard` extra rows before and
+    after and ldc - N padding columns, all pre-filled with a NaN sentinel.
+    Returns (C window, whole C buffer, window row offset)."""
+    dt = torch.float32 if a.dtype == np.float32 else torch.bfloat16
+    ldc = ldc or N
+    da, db = to_dev(a), to_dev(b)
+    rows = M + 2 * guard
+    buf = torch.full((max(rows, 1), max(ldc, 1)), float("nan"), dtype=dt, device="cuda")
+    c_ptr = buf.data_ptr() + guard * ldc * buf.element_size()
+    args = (da.data_ptr(), db.data_ptr(), c_ptr, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+    if dt == torch.float32:
+        rc = mm.mmrelu_f32(*args) if variant is None else mm.mmrelu_f32_variant(variant, *args)
+    else:
+        rc = mm.mmrelu_bf16(*args) if variant is None else mm.mmrelu_bf16_variant(variant, *args)
+    assert rc == mm.MMRELU_OK, mm.status_string(rc)
+    torch.cuda.synchronize()
+    whole = to_host(buf)
+    win = whole[guard:guard + M, :N] if M > 0 else whole[:0, :N]
+    return win, whole
+
+
+def check_f32(c, r, K):
+    assert np.all(np.isfinite(c))
+    err = np.abs(c.astype(np.float64) - r)
+    assert err.max(initial=0) <= F32_TOL(K), f"max err {err.max()} > {F32_TOL(K)}"
+    assert np.all(c >= 0)
+
+
+def check_bf16(c_bits, r):
+    c = datagen.bf16_bits_to_f32(c_bits).astype(np.float64)
+    assert np.all(np.isfinite(c)) and np.all(c >= 0)
+    nr = np.linalg.norm(r)
+    rel = np.linalg.norm(c - r) / nr if nr > 0 else np.linalg.norm(c)
+    assert rel <= 1e-2, f"relative Frobenius error {rel}"
+    assert np.all(np.abs(c - r) <= 2.0 ** -8 * np.abs(r) + 1e-6)
+
+
+def variants(dtype):
+    return list(range(mm.mmrelu_num_variants(dtype)))
+
+
+def accepts(dtype, v, N, K, lda, ldb, ldc):
+    name = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)["name"]
+    if "simple" in name or "unaligned" in name:
+        return True
+    q = 4 if dtype == mm.DTYPE_F32 else 8
+    return all(x % q == 0 for x in (N, K, lda, ldb, ldc))
+
+
+F32_SHAPES = [  # (M, N, K) spanning several tiles with ragged tails, plus degenerate ones
+    (1, 1, 1), (3, 5, 7), (17, 33, 65), (129, 131, 67), (257, 260, 132), (300, 264, 516),
+    (64, 64, 64), (128, 256, 96), (260, 4, 12), (4, 260, 8), (513, 129, 33),
+]
+BF16_SHAPES = [
+    (8, 8, 8), (1, 8, 8), (264, 520, 136), (256, 256, 64), (300, 264, 72), (520, 8, 200),
+    (16, 512, 1032), (3, 5, 7), (257, 131, 67),
+]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("variant", variants(mm.DTYPE_F32))
+def test_f32_variants_small(variant, shape):
+    M, N, K = shape
+    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N):
+        pytest.skip("variant needs 16-byte rows")
+    a = datagen.normal_f32(10 + M, M, K, 1 / math.sqrt(K))
+    b = datagen.normal_f32(20 + N, K, N, 1 / math.sqrt(K))
+    c, _ = run(a, b, M, N, K, K, N, variant=variant)
+    check_f32(c, oracle.mmrelu(a, b), K)
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("variant", variants(mm.DTYPE_BF16))
+def test_bf16_variants_small(variant, shape):
+    M, N, K = shape
+    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N):
+        pytest.skip("variant needs 16-byte rows")
+    a = datagen.f32_to_bf16_bits(datagen.normal_f32(30 + M, M, K, 1 / math.sqrt(K)))
+    b = datagen.f32_to_bf16_bits(datagen.normal_f32(40 + N, K, N, 1 / math.sqrt(K)))
+    c, _ = run(a, b, M, N, K, K, N, variant=variant)
+    check_bf16(c, oracle.mmrelu(a, b))
+
+
+@pytest.mark.parametrize("variant", variants(mm.DTYPE_F32))
+def test_f32_exact_integers_bit_exact(variant):
+    M, N, K = 200, 132, 300
+    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N):
+        pytest.skip("variant needs 16-byte rows")
+    a = datagen.small_int_f32(51, M, K)
+    b = datagen.small_int_f32(52, K, N)
+    c, _ = run(a, b, M, N, K, K, N, variant=variant)
+    np.testing.assert_array_equal(c.astype(np.float64), oracle.mmrelu(a, b))
+
+
+@pytest.mark.parametrize("variant", variants(mm.DTYPE_BF16))
+def test_bf16_exact_integers_round_to_nearest_even(variant):
+    """Integer inputs: fp32 accumulation is exact, so C must equal the oracle
+    rounded to bf16 (nearest, ties to even) bit for bit: pins the epilogue
+    rounding mode."""
+    M, N, K = 136, 264, 520
+    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N):
+        pytest.skip("variant needs 16-byte rows")
+    a = datagen.f32_to_bf16_bits(datagen.small_int_f32(61, M, K))
+    b = datagen.f32_to_bf16_bits(datagen.small_int_f32(62, K, N))
+    r = oracle.mmrelu(a, b)
+    assert np.abs(r).max() > 256          # results need more than bf16's 8 bits
+    c, _ = run(a, b, M, N, K, K, N, variant=variant)
+    np.testing.assert_array_equal(c, bf16_round_ref(r))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_band_and_padded_leading_dimensions(dtype):
+    """Masked store: nothing outside the M x N window is written, with padded
+    lda/ldb/ldc (multiples of 8 so every variant applies) and rows around C."""
+    M, N, K = 131, 264, 72
+    lda, ldb, ldc = K + 8, N + 16, N + 24
+    a32 = datagen.pad_rows(datagen.normal_f32(71, M, K, 1 / math.sqrt(K)), lda, fill=np.nan)
+    b32 = datagen.pad_rows(datagen.normal_f32(72, K, N, 1 / math.sqrt(K)), ldb, fill=np.nan)
+    if dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a32), datagen.f32_to_bf16_bits(b32)
+        dt = mm.DTYPE_BF16
+    else:
+        a, b, dt = a32, b32, mm.DTYPE_F32
+    r = oracle.mmrelu(a, b, M=M, N=N, K=K, lda=lda, ldb=ldb)
+    for v in variants(dt):
+        assert accepts(dt, v, N, K, lda, ldb, ldc)
+        c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, variant=v, guard=3)
+        if dtype == "bf16":
+            check_bf16(c, r)
+            wf = datagen.bf16_bits_to_f32(whole)
+        else:
+            check_f32(c, r, K)
+            wf = whole
+        outside = np.ones(wf.shape, bool)
+        outside[3:3 + M, :N] = False
+        assert np.all(np.isnan(wf[outside])), f"variant {v} wrote outside the window"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_k_zero_writes_zeros(dtype):
+    M, N = 70, 136
+    a = np.zeros((M, 1), np.float32 if dtype == "f32" else np.uint16)
+    b = np.zeros((1, N), a.dtype)
+    c, _ = run(a, b, M, N, 0, 1, N)
+    assert np.all(c == 0)
+
+
+def test_empty_outputs_launch_nothing():
+    t = torch.zeros(4, 4, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert mm.mmrelu_f32(t.data_ptr(), t.data_ptr(), t.data_ptr(), 0, 4, 4, 4, 4, 4, s) == 0
+    assert mm.mmrelu_f32(t.data_ptr(), t.data_ptr(), t.data_ptr(), 4, 0, 4, 4, 4, 4, s) == 0
+    torch.cuda.synchronize()
+    assert torch.all(t == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic_repeats(dtype):
+    """No atomics: 20 runs must agree bit for bit (a proxy for LDS races)."""
+    M, N, K = 512, 512, 1024
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    a = to_dev(datagen.normal_f32(81, M, K, 1 / math.sqrt(K))).to(tdt)
+    b = to_dev(datagen.normal_f32(82, K, N, 1 / math.sqrt(K))).to(tdt)
+    first = mm.mmrelu(a, b).clone()
+    for _ in range(19):
+        assert torch.equal(mm.mmrelu(a, b), first)
+
+
+def test_torch_wrapper_row_strided_out():
+    M, N, K = 96, 136, 40
+    a = datagen.normal_f32(91, M, K)
+    b = datagen.normal_f32(92, K, N)
+    big = torch.full((M, N + 8), -1.0, device="cuda")
+    out = big[:, :N]
+    mm.mmrelu(to_dev(a), to_dev(b), out=out)
+    torch.cuda.synchronize()
+    check_f32(out.cpu().numpy(), oracle.mmrelu(a, b), K)
+    assert torch.all(big[:, N:] == -1.0)
+
+
+# --- the five workloads at full size -----------------------------------------
+
+def sample_indices(M, N, seed, rows=6, cols=6, points=4000):
+    """Whole rows (first, last, random), whole columns (likewise) and random
+    entries of an M x N output, as flat (row, col) index arrays."""
+    rng = np.random.default_rng(seed)
+    rsel = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, rows)]))
+    csel = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, cols)]))
+    ii = np.concatenate([np.repeat(rsel, N), np.tile(np.arange(M), csel.size), rng.integers(0, M, points)])
+    jj = np.concatenate([np.tile(np.arange(N), rsel.size), np.repeat(csel, M), rng.integers(0, N, points)])
+    return ii, jj
+
+
+@pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
+def test_workload_full_size(ident):
+    cfg = datagen.CONFIGS[ident]
+    print(f"workload {cfg.name}", flush=True)
+    a, b = datagen.make_inputs(cfg)
+    c, _ = run(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, ldc=cfg.ldc)
+    if cfg.M * cfg.N * cfg.K <= 1024 ** 3:
+        r = oracle.mmrelu(a, b, M=cfg.M, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
+        cs, rs = c, r
+    else:
+        ii, jj = sample_indices(cfg.M, cfg.N, 1000 + ident)
+        rs = oracle.mmrelu_at(a, b, ii, jj, cfg.K, cfg.lda, cfg.ldb)
+        cs = c[ii, jj]
+    if cfg.dtype == "f32":
+        check_f32(cs, rs, cfg.K)
+        cfull = c
+    else:
+        check_bf16(cs, rs)
+        cfull = datagen.bf16_bits_to_f32(c)
+    # any-size properties over the whole output: finite, non-negative, and
+    # for inputs symmetric about 0 about half the outputs are exactly zero
+    assert np.all(np.isfinite(cfull)) and np.all(cfull >= 0)
+    frac = float(np.mean(cfull == 0))
+    assert abs(frac - 0.5) < 0.01, frac

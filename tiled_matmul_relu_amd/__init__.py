@@ -1,0 +1,191 @@
+"""Python binding of libmmrelu, the gfx950 library computing C = relu(A·B).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmmrelu.so`` (built from ``csrc/`` by ``build.py``). The C
+entry points (``include/mmrelu.h``) are exposed under the same names and take
+raw device pointers, sizes, leading dimensions (elements) and a HIP stream
+handle. ``mmrelu(a, b, out=None)`` is a convenience wrapper for torch device
+tensors (row-major, unit column stride) that launches on torch's current
+stream; torch only provides device memory and streams.
+
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmmrelu.so")
+
+MMRELU_OK = 0
+MMRELU_ERR_INVALID_VALUE = 1
+MMRELU_ERR_NULL_POINTER = 2
+MMRELU_ERR_MISALIGNED = 3
+MMRELU_ERR_LAUNCH = 4
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+EXPORTED = (
+    "mmrelu_f32", "mmrelu_bf16", "mmrelu_status_string", "mmrelu_version",
+    "mmrelu_plan", "mmrelu_num_variants", "mmrelu_plan_variant",
+    "mmrelu_wave_quantization", "mmrelu_f32_variant", "mmrelu_bf16_variant",
+)
+
+
+class MmreluError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("threads", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32),
+        ("cus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64),
+        ("waves", ctypes.c_int64), ("idle_slots_last", ctypes.c_int64), ("name", ctypes.c_char * 64),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d["name"] = self.name.decode()
+        return d
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libmmrelu.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m tiled_matmul_relu_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    for name in ("mmrelu_f32", "mmrelu_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    for name in ("mmrelu_f32_variant", "mmrelu_bf16_variant"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    lib.mmrelu_status_string.argtypes = [ctypes.c_int]
+    lib.mmrelu_status_string.restype = ctypes.c_char_p
+    lib.mmrelu_version.restype = ctypes.c_char_p
+    lib.mmrelu_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i32, ctypes.POINTER(Plan)]
+    lib.mmrelu_plan.restype = ctypes.c_int
+    lib.mmrelu_plan_variant.argtypes = [ctypes.c_int, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.POINTER(Plan)]
+    lib.mmrelu_plan_variant.restype = ctypes.c_int
+    lib.mmrelu_num_variants.argtypes = [ctypes.c_int]
+    lib.mmrelu_num_variants.restype = ctypes.c_int
+    lib.mmrelu_wave_quantization.argtypes = [i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.mmrelu_wave_quantization.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mmrelu_status_string(status).decode()
+
+
+def version() -> str:
+    return load_library().mmrelu_version().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MMRELU_OK:
+        raise MmreluError(status, where)
+
+
+# --- C entry points with the same names (raw pointers) -----------------------
+
+def mmrelu_f32(A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+               stream: int = 0) -> int:
+    """Enqueue C = relu(A·B), fp32. Pointers are device addresses; returns the status."""
+    return load_library().mmrelu_f32(A, B, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_bf16(A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                stream: int = 0) -> int:
+    """Enqueue C = relu(A·B), bf16 in/out, fp32 accumulation; returns the status."""
+    return load_library().mmrelu_bf16(A, B, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_f32_variant(variant: int, A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                       ldc: int, stream: int = 0) -> int:
+    return load_library().mmrelu_f32_variant(variant, A, B, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_bf16_variant(variant: int, A: int, B: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                        ldc: int, stream: int = 0) -> int:
+    return load_library().mmrelu_bf16_variant(variant, A, B, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_plan(dtype: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, cus: int = 0) -> dict:
+    p = Plan()
+    _check(load_library().mmrelu_plan(dtype, M, N, K, lda, ldb, ldc, cus, ctypes.byref(p)), "mmrelu_plan")
+    return p.as_dict()
+
+
+def mmrelu_plan_variant(dtype: int, variant: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                        cus: int = 0) -> dict:
+    p = Plan()
+    _check(load_library().mmrelu_plan_variant(dtype, variant, M, N, K, lda, ldb, ldc, cus, ctypes.byref(p)),
+           "mmrelu_plan_variant")
+    return p.as_dict()
+
+
+def mmrelu_num_variants(dtype: int) -> int:
+    return load_library().mmrelu_num_variants(dtype)
+
+
+def mmrelu_wave_quantization(blocks: int, slots: int) -> tuple[int, int]:
+    w, idle = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().mmrelu_wave_quantization(blocks, slots, ctypes.byref(w), ctypes.byref(idle)),
+           "mmrelu_wave_quantization")
+    return w.value, idle.value
+
+
+# --- torch convenience wrapper ----------------------------------------------
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("matrices must be 2-D, row-major with unit column stride")
+    return max(t.stride(0), t.shape[1], 1)
+
+
+def mmrelu(a, b, out=None, variant: int | None = None, stream=None):
+    """relu(a @ b) for torch device tensors (float32 or bfloat16, row-major).
+
+    ``out`` may be a preallocated (M, N) tensor (possibly a row-strided view).
+    Launches on ``stream`` (default: torch's current stream) and returns
+    ``out`` without synchronising."""
+    import torch
+    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("a and b must both be float32 or both bfloat16")
+    if not (a.is_cuda and b.is_cuda):
+        raise ValueError("a and b must be device tensors")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif out.shape != (M, N) or out.dtype != a.dtype or out.device != a.device:
+        raise ValueError("out has the wrong shape, dtype or device")
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    args = (a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _ld(a), _ld(b), _ld(out), s.cuda_stream)
+    if a.dtype == torch.float32:
+        rc = mmrelu_f32(*args) if variant is None else mmrelu_f32_variant(variant, *args)
+    else:
+        rc = mmrelu_bf16(*args) if variant is None else mmrelu_bf16_variant(variant, *args)
+    _check(rc, "mmrelu")
+    return out

@@ -1,0 +1,127 @@
+// Device-side helpers shared by the matrix-core kernels: buffer resources
+// with hardware range checking, direct global->LDS loads, wait counters,
+// and the workgroup -> output-tile mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mmrelu {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define MMRELU_LDS __attribute__((address_space(3)))
+
+// Data-format word of a gfx9 buffer resource (32-bit untyped elements).
+constexpr uint32_t kBufferFormat = 0x00020000u;
+// Per-lane offset that is always past a resource's range: loads return 0
+// (direct-to-LDS loads write 0) and stores are dropped.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Largest byte range given to one resource; every valid per-lane offset is
+// below it, so kOutOfRange is never inside a range.
+constexpr int64_t kMaxRange = 0x7FFFFF00;
+
+// Buffer resource over [base, base + bytes) as four scalar words (base
+// address, stride 0, byte range, data format); bytes is clamped to kMaxRange.
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    rsrc_t r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((a >> 32) & 0xFFFF));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n));
+    r[3] = static_cast<int32_t>(kBufferFormat);
+    return r;
+}
+
+// LDS byte address of a __shared__ object (for M0).
+template <typename T>
+__device__ inline uint32_t lds_address(const T *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const MMRELU_LDS T *)p));
+}
+
+// Direct global -> LDS copy: lane l writes 16 (or 4) bytes at LDS byte
+// address lds + l * 16 (or 4); `lds` must be wave-uniform, `soffset` is a
+// uniform byte offset added to every lane's voffset. A lane whose offset is
+// out of the resource's range writes zeros.
+//
+// Issued as inline assembly on purpose: the compiler cannot tell which LDS
+// bytes such a copy writes, and for the builtin it waits for every copy in
+// flight before any later LDS read, which would serialise the prefetch of
+// slab k+1 with the multiply of slab k. Completion is awaited explicitly
+// (wait_vmcnt + barrier) before a stage is read; the "memory" clobber keeps
+// the compiler from moving LDS accesses across the copy.
+// M0 is declared clobbered; the kernels make no other use of M0 (no LDS
+// builtins that take it, no dynamic register indexing).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int Bytes>
+__device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uint32_t soffset = 0)
+{
+    static_assert(Bytes == 4 || Bytes == 16, "4- or 16-byte lanes");
+    if constexpr (Bytes == 16)
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                     :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
+                     :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Store resource over [base, base + bytes) for the masked epilogue stores:
+// lanes with an out-of-range offset store nothing.
+__device__ inline __amdgpu_buffer_rsrc_t make_store_rsrc(void *base, int64_t bytes)
+{
+    const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(n), kBufferFormat);
+}
+__device__ inline void store_b128(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voffset, 0, 0);
+}
+__device__ inline void store_b64(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voffset, 0, 0);
+}
+__device__ inline void store_b32(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, voffset, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their "no wait" maxima).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup id -> (tile_m, tile_n). Consecutive workgroup ids go to the 8
+// XCDs in turn, each with its own L2, so ids are first regrouped so that each
+// XCD owns a contiguous range of logical tiles; that range is then walked in
+// bands of `group_m` tile-rows, column by column inside a band, so the tiles
+// resident on one XCD at a time share A row-panels and B column-panels.
+__device__ inline void tile_of(int64_t id, int64_t grid, int tiles_m, int tiles_n, int group_m,
+                               int &tm, int &tn)
+{
+    constexpr int kXcds = 8;
+    int64_t lid = id;
+    const int64_t per = grid / kXcds;
+    if (per > 0 && id < per * kXcds) lid = (id % kXcds) * per + id / kXcds;
+    const int64_t band = static_cast<int64_t>(group_m) * tiles_n;
+    const int64_t first_m = (lid / band) * group_m;
+    const int64_t rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int64_t in_band = lid % band;
+    tm = static_cast<int>(first_m + in_band % rows);
+    tn = static_cast<int>(in_band / rows);
+}
+
+}  // namespace mmrelu

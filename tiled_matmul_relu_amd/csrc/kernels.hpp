@@ -1,0 +1,41 @@
+// Launch interface shared by the kernel translation units and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mmrelu {
+
+// Validated problem description handed to every launcher. Sizes fit int32
+// (checked by the C-ABI layer); leading dimensions are in elements.
+struct Problem {
+    const void *A;
+    const void *B;
+    void *C;
+    int32_t M, N, K;
+    int64_t lda, ldb, ldc;
+};
+
+// Launches one variant over `grid` workgroups on `stream`; returns the launch
+// status (hipGetLastError right after the launch).
+using Launcher = hipError_t (*)(const Problem &, int64_t grid, hipStream_t stream);
+
+struct Variant {
+    const char *name;     // kernel symbol family, as a profiler shows it
+    int dtype;            // MMRELU_DTYPE_*
+    int block_m, block_n, block_k;
+    int threads;
+    int wg_per_cu;        // resident workgroups per CU (register / LDS bound)
+    int align_elems;      // 0: any layout; else lda, ldb, ldc, K, N must be
+                          // multiples of this and A, B, C 16-byte aligned
+    Launcher launch;
+};
+
+// Kernel variants, defined in the kernel translation units (host functions
+// returning static descriptors).
+const Variant *variant_f32_simple();
+const Variant *variant_bf16_simple();
+const Variant *variant_f32_mfma128();
+const Variant *variant_f32_mfma128_unaligned();
+const Variant *variant_bf16_mfma256();
+
+}  // namespace mmrelu

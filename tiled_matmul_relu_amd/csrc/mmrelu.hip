@@ -1,0 +1,236 @@
+// C-ABI layer of libmmrelu: argument checks, the planner (kernel variant,
+// grid, wave quantisation over the compute units) and the launch on the
+// caller's stream. Declarations and the full contract are in mmrelu.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mmrelu.h"
+#include "kernels.hpp"
+
+namespace mmrelu {
+namespace {
+
+// Kernel tables in a fixed order (the variant index of the C-ABI).
+constexpr int kNumF32 = 3;
+constexpr int kNumBf16 = 2;
+const Variant *const *f32_table()
+{
+    static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
+                                              variant_f32_mfma128_unaligned()};
+    return t;
+}
+const Variant *const *bf16_table()
+{
+    static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256()};
+    return t;
+}
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxLd = int64_t{1} << 21;
+constexpr int kDefaultCus = 256;
+
+const Variant *variant_at(int dtype, int32_t v)
+{
+    if (dtype == MMRELU_DTYPE_F32 && v >= 0 && v < kNumF32) return f32_table()[v];
+    if (dtype == MMRELU_DTYPE_BF16 && v >= 0 && v < kNumBf16) return bf16_table()[v];
+    return nullptr;
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K < 0) return MMRELU_ERR_INVALID_VALUE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMRELU_ERR_INVALID_VALUE;
+    if (lda < std::max<int64_t>(1, K) || ldb < std::max<int64_t>(1, N) || ldc < std::max<int64_t>(1, N))
+        return MMRELU_ERR_INVALID_VALUE;
+    if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return MMRELU_ERR_INVALID_VALUE;
+    return MMRELU_OK;
+}
+
+int check_pointers(const void *A, const void *B, const void *C, int64_t M, int64_t N, int64_t K, size_t esize)
+{
+    if (M == 0 || N == 0) return MMRELU_OK;
+    if (C == nullptr) return MMRELU_ERR_NULL_POINTER;
+    if (K > 0 && (A == nullptr || B == nullptr)) return MMRELU_ERR_NULL_POINTER;
+    auto misaligned = [esize](const void *p) { return (reinterpret_cast<uintptr_t>(p) % esize) != 0; };
+    if (misaligned(C) || (K > 0 && (misaligned(A) || misaligned(B)))) return MMRELU_ERR_MISALIGNED;
+    return MMRELU_OK;
+}
+
+// Compute-unit count of the current device, cached per device id.
+int device_cus()
+{
+    static std::atomic<int> cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return kDefaultCus;
+    }
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = kDefaultCus;
+    }
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                 const void *A, const void *B, const void *C)
+{
+    if (v->align_elems == 0) return true;
+    const int64_t q = v->align_elems;
+    if (N % q || K % q || lda % q || ldb % q || ldc % q) return false;
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    return al16(A) && al16(B) && al16(C);
+}
+
+// Planner: the default variant for a dtype and shape. Pointers are taken as
+// 16-byte aligned when null (planning without buffers).
+int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                       const void *A, const void *B, const void *C)
+{
+    (void)M;
+    if (dtype == MMRELU_DTYPE_F32)
+        return layout_fits(f32_table()[1], N, K, lda, ldb, ldc, A, B, C) ? 1 : 2;
+    return layout_fits(bf16_table()[1], N, K, lda, ldb, ldc, A, B, C) ? 1 : 0;
+}
+
+int fill_plan(const Variant *v, int32_t index, int64_t M, int64_t N, int32_t cus, mmrelu_plan_t *out)
+{
+    mmrelu_plan_t p;
+    std::memset(&p, 0, sizeof p);
+    p.variant = index;
+    p.block_m = v->block_m;
+    p.block_n = v->block_n;
+    p.block_k = v->block_k;
+    p.threads = v->threads;
+    p.wg_per_cu = v->wg_per_cu;
+    p.cus = cus;
+    p.tiles_m = (M + v->block_m - 1) / v->block_m;
+    p.tiles_n = (N + v->block_n - 1) / v->block_n;
+    p.grid = p.tiles_m * p.tiles_n;
+    // one launch holds fewer than 2^32 work-items
+    if (p.grid * v->threads >= (int64_t{1} << 32)) return MMRELU_ERR_INVALID_VALUE;
+    if (p.grid > 0) {
+        int rc = mmrelu_wave_quantization(p.grid, int64_t{cus} * v->wg_per_cu, &p.waves, &p.idle_slots_last);
+        if (rc != MMRELU_OK) return rc;
+    }
+    std::snprintf(p.name, sizeof p.name, "%s", v->name);
+    *out = p;
+    return MMRELU_OK;
+}
+
+int run(int dtype, int32_t variant, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+        int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    const size_t esize = dtype == MMRELU_DTYPE_F32 ? 4 : 2;
+    int rc = check_shape(M, N, K, lda, ldb, ldc);
+    if (rc != MMRELU_OK) return rc;
+    rc = check_pointers(A, B, C, M, N, K, esize);
+    if (rc != MMRELU_OK) return rc;
+    if (variant < 0) variant = choose_variant(dtype, M, N, K, lda, ldb, ldc, A, B, C);
+    const Variant *v = variant_at(dtype, variant);
+    if (v == nullptr) return MMRELU_ERR_INVALID_VALUE;
+    if (K > 0 && !layout_fits(v, N, K, lda, ldb, ldc, A, B, C)) return MMRELU_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return MMRELU_OK;
+    mmrelu_plan_t plan;
+    rc = fill_plan(v, variant, M, N, kDefaultCus, &plan);
+    if (rc != MMRELU_OK) return rc;
+    Problem p{A, B, C, static_cast<int32_t>(M), static_cast<int32_t>(N), static_cast<int32_t>(K), lda, ldb, ldc};
+    hipError_t e = v->launch(p, plan.grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MMRELU_OK : MMRELU_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace mmrelu
+
+using namespace mmrelu;
+
+extern "C" {
+
+int mmrelu_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    return run(MMRELU_DTYPE_F32, -1, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    return run(MMRELU_DTYPE_BF16, -1, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_f32_variant(int32_t variant, const float *A, const float *B, float *C, int64_t M, int64_t N,
+                       int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return run(MMRELU_DTYPE_F32, variant, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_bf16_variant(int32_t variant, const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M,
+                        int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return run(MMRELU_DTYPE_BF16, variant, A, B, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+const char *mmrelu_status_string(int status)
+{
+    switch (status) {
+    case MMRELU_OK: return "ok";
+    case MMRELU_ERR_INVALID_VALUE: return "invalid value (size, leading dimension or variant)";
+    case MMRELU_ERR_NULL_POINTER: return "null pointer";
+    case MMRELU_ERR_MISALIGNED: return "pointer not aligned to its element size";
+    case MMRELU_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *mmrelu_version(void) { return "mmrelu 0.1 (gfx950)"; }
+
+int mmrelu_num_variants(int dtype)
+{
+    if (dtype == MMRELU_DTYPE_F32) return kNumF32;
+    if (dtype == MMRELU_DTYPE_BF16) return kNumBf16;
+    return 0;
+}
+
+int mmrelu_wave_quantization(int64_t blocks, int64_t slots, int64_t *waves, int64_t *idle_last)
+{
+    if (blocks < 0 || slots < 1 || waves == nullptr || idle_last == nullptr) return MMRELU_ERR_INVALID_VALUE;
+    const int64_t w = (blocks + slots - 1) / slots;
+    *waves = w;
+    *idle_last = w * slots - blocks;
+    return MMRELU_OK;
+}
+
+int mmrelu_plan_variant(int dtype, int32_t variant, int64_t M, int64_t N, int64_t K, int64_t lda,
+                        int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out)
+{
+    if (out == nullptr) return MMRELU_ERR_NULL_POINTER;
+    int rc = check_shape(M, N, K, lda, ldb, ldc);
+    if (rc != MMRELU_OK) return rc;
+    const Variant *v = variant_at(dtype, variant);
+    if (v == nullptr || cus < 0) return MMRELU_ERR_INVALID_VALUE;
+    return fill_plan(v, variant, M, N, cus > 0 ? cus : device_cus(), out);
+}
+
+int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                int32_t cus, mmrelu_plan_t *out)
+{
+    if (dtype != MMRELU_DTYPE_F32 && dtype != MMRELU_DTYPE_BF16) return MMRELU_ERR_INVALID_VALUE;
+    int rc = check_shape(M, N, K, lda, ldb, ldc);
+    if (rc != MMRELU_OK) return rc;
+    return mmrelu_plan_variant(dtype, choose_variant(dtype, M, N, K, lda, ldb, ldc, nullptr, nullptr, nullptr), M,
+                               N, K, lda, ldb, ldc, cus, out);
+}
+
+}  // extern "C"
