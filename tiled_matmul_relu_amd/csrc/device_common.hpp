@@ -59,7 +59,9 @@ __device__ inline uint32_t lds_address(const T *p)
 // (wait_vmcnt + barrier) before a stage is read; the "memory" clobber keeps
 // the compiler from moving LDS accesses across the copy.
 // M0 is declared clobbered; the kernels make no other use of M0 (no LDS
-// builtins that take it, no dynamic register indexing).
+// builtins that take it, no dynamic register indexing). An LDS copy must not
+// directly follow the SALU write of M0 (one wait state, as the compiler
+// itself inserts for the builtin form), hence the s_nop.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int Bytes>
@@ -67,10 +69,10 @@ __device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uin
 {
     static_assert(Bytes == 4 || Bytes == 16, "4- or 16-byte lanes");
     if constexpr (Bytes == 16)
-        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
                      :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
                      :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
 }
 #pragma clang diagnostic pop

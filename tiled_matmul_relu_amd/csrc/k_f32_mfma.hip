@@ -226,7 +226,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 2) void mmrelu_f32_mfma(
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t off =
                         (row_ok && n0 + col + r < N) ? static_cast<uint32_t>((row * ldc + col + r) * 4) : kOutOfRange;
-                    store_b32(rc, off, __builtin_bit_cast(uint32_t, v[r]));
+                    store_b32(rc, off, __float_as_uint(v[r]));
                 }
             }
         }
