@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32 4096^3 workload")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a kernel of known traffic, "
+                         "for scaling memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,6 +165,14 @@ def main():
                             "frac": round(r32["tflops"] / PEAK_TFLOPS["f32"], 4), "peak": PEAK_TFLOPS["f32"],
                             "kernel": r32["plan"]["name"],
                             "traffic": measured_traffic("f32", r32["plan"]["name"])}
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n * 4
     if not args.no_cpu_baseline:
         import oracle
         a, b = res["inputs"]

@@ -29,6 +29,16 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-file compiler options. The bf16 kernel keeps 256 accumulators per lane
+# in AGPRs next to two register sets of fragments; the default scheduler then
+# shuffles accumulators between AGPRs inside the K loop (hundreds of
+# v_accvgpr moves per iteration), while the register-pressure-first strategy
+# keeps every MFMA's accumulator in place.
+FILE_FLAGS = {
+    "k_bf16_mfma.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -38,7 +48,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -68,6 +68,12 @@ template <int Bytes>
 __device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uint32_t soffset = 0)
 {
     static_assert(Bytes == 4 || Bytes == 16, "4- or 16-byte lanes");
+    // Both scalar operands are wave-uniform; keep them in SGPRs even when
+    // they are compile-time constants (a buffer soffset literal outside the
+    // inline-constant range is not encodable).
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    soffset = __builtin_amdgcn_readfirstlane(soffset);
+    asm("" : "+s"(lds), "+s"(soffset));
     if constexpr (Bytes == 16)
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
                      :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");

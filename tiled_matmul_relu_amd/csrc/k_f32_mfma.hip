@@ -53,9 +53,10 @@ struct F32Tile {
     static_assert(kLoadsB * kLaneBytes * 64 * kWaves == BK * BN * 4, "B load split");
 };
 
-// A: row r's chunk c sits at c ^ swz_a(r); 16 consecutive rows read at one
-// logical chunk land on distinct banks for 32- or 64-bank LDS.
-__device__ inline int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// A: row r's chunk c sits at c ^ (r % 8); the 16 lanes of a ds_read_b128
+// that read one logical chunk of 16 consecutive rows then run at the full
+// LDS rate (measured on gfx950).
+__device__ inline int swz_a(int r) { return r & 7; }
 // B: row k's chunk c sits at c ^ swz_b(k); the four rows k, k+4, k+8, k+12
 // read together by one ds_read_b32 land in different 64-byte quarters.
 __device__ inline int swz_b(int k) { return ((k >> 2) & 3) << 2; }
