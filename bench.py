@@ -27,7 +27,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "bf16": ["tiled_matmul_relu_amd/csrc/k_bf16_mfma.hip", "tiled_matmul_relu_amd/csrc/device_common.hpp"],
+    "bf16": ["tiled_matmul_relu_amd/csrc/k_bf16_pingpong.hip", "tiled_matmul_relu_amd/csrc/device_common.hpp"],
     "f32": ["tiled_matmul_relu_amd/csrc/k_f32_mfma.hip", "tiled_matmul_relu_amd/csrc/device_common.hpp"],
 }
 

@@ -108,7 +108,7 @@ def test_plans_for_the_workloads():
     assert p["tiles_m"] == -(-4097 // p["block_m"]) and p["tiles_n"] == -(-3001 // p["block_n"])
     # 8192^3 bf16: matrix-core kernel, whole waves
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 8192, 8192, 8192, 8192, 8192, 8192, cus=256)
-    assert "bf16_mfma" in p["name"] and p["idle_slots_last"] == 0
+    assert "bf16_pingpong" in p["name"] and p["idle_slots_last"] == 0
     # bf16 with an odd leading dimension falls back to the plain tiled kernel
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 100, 100, 100, 100, 100, 100, cus=256)
     assert "simple" in p["name"]

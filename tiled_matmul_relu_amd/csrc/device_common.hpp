@@ -73,6 +73,8 @@ __device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uin
     // inline-constant range is not encodable).
     lds = __builtin_amdgcn_readfirstlane(lds);
     soffset = __builtin_amdgcn_readfirstlane(soffset);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
     asm("" : "+s"(lds), "+s"(soffset));
     if constexpr (Bytes == 16)
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"

@@ -66,7 +66,7 @@ struct Bf16Tile {
 // full rate on gfx950).
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m)
@@ -118,11 +118,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     // the B resource of that slab. Every lane is masked (a slab at or past K
     // only zero-fills a stage that is never read), so the main loop has no
     // branches and every slab costs the same vmcnt count.
-    auto b_rsrc = [&](int k0) {
+    auto b_rsrc = [&](int k0) __attribute__((always_inline)) {
         return make_rsrc(B + static_cast<int64_t>(k0) * ldb + n0,
                          ((static_cast<int64_t>(K) - 1 - k0) * ldb + N - n0) * 2);
     };
-    auto issue_copy = [&](int q, int stage, int k0, const rsrc_t &rb) {
+    auto issue_copy = [&](int q, int stage, int k0, const rsrc_t &rb) __attribute__((always_inline)) {
         const uint32_t la = lds0 + stage * (T::kStage * 2);
         if (q < T::kLoadsA) {
             const uint32_t off = (a_col[q] < K - k0) ? a_voff[q] : kOutOfRange;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
             load_to_lds<16>(rb, la + T::kStageA * 2 + (qb * T::kWaves + wave) * 1024, b_voff[qb]);
         }
     };
-    auto issue_loads = [&](int stage, int k0) {
+    auto issue_loads = [&](int stage, int k0) __attribute__((always_inline)) {
         const rsrc_t rb = b_rsrc(k0);
 #pragma unroll
         for (int q = 0; q < T::kLoads; ++q) issue_copy(q, stage, k0, rb);
@@ -162,14 +162,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
 
     // Two register sets of MFMA operands: while the MFMAs of slab kt run, the
     // fragments of slab kt+1 are read from LDS.
-    bf16x8 fa[2][T::MB], fb[2][T::NB];
+    bf16x8 fa[PREFETCH ? 2 : 1][T::MB], fb[PREFETCH ? 2 : 1][T::NB];
     // Fragment reads of one 16-row A block (c < MB) or one 16-column B block
     // (c < NB) of a stage into register set `set`.
-    auto load_frag_a = [&](int set, int stage, int c) {
+    auto load_frag_a = [&](int set, int stage, int c) __attribute__((always_inline)) {
         const uint16_t *st = lds + stage * T::kStage;
         fa[set][c] = *reinterpret_cast<const bf16x8 *>(st + a_off + c * 16 * BK);
     };
-    auto load_frag_b = [&](int set, int stage, int c) {
+    auto load_frag_b = [&](int set, int stage, int c) __attribute__((always_inline)) {
         const uint16_t *st = lds + stage * T::kStage;
         i16x4 half[2];
 #pragma unroll
@@ -177,13 +177,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
             half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(st + b_off[c] + 4 * h * BN));
         fb[set][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto load_frags = [&](int set, int stage) {
+    auto load_frags = [&](int set, int stage) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < T::NB; ++c) load_frag_b(set, stage, c);
 #pragma unroll
         for (int c = 0; c < T::MB; ++c) load_frag_a(set, stage, c);
     };
-    auto mfmas = [&](int set) {
+    auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < T::MB; ++i)
 #pragma unroll
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     // move the next step's MFMAs above the barrier, right behind the reads
     // that feed them.
     constexpr int kChunks = (T::MB > T::NB ? T::MB : T::NB) > T::kLoads ? (T::MB > T::NB ? T::MB : T::NB) : T::kLoads;
-    auto step = [&](int kt, int set) {
+    auto step = [&](int kt, int set) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(STAGES - 2) * T::kLoads>();
         __syncthreads();
@@ -239,22 +239,41 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     };
 
     const int nk = (K + BK - 1) / BK;
-    if (nk > 0) {
+    if constexpr (PREFETCH) {
+        if (nk > 0) {
 #pragma unroll
-        for (int s = 0; s < STAGES; ++s) issue_loads(s, s * BK);
-        wait_vmcnt<(STAGES - 1) * T::kLoads>();
-        __syncthreads();
-        load_frags(0, 0);
-        int kt = 0;
-        for (; kt + 2 < nk; kt += 2) {
-            step(kt, 0);
-            step(kt + 1, 1);
+            for (int s = 0; s < STAGES; ++s) issue_loads(s, s * BK);
+            wait_vmcnt<(STAGES - 1) * T::kLoads>();
+            __syncthreads();
+            load_frags(0, 0);
+            int kt = 0;
+            for (; kt + 2 < nk; kt += 2) {
+                step(kt, 0);
+                step(kt + 1, 1);
+            }
+            if (kt + 1 < nk) {
+                step(kt, 0);
+                mfmas(1);
+            } else {
+                mfmas(0);
+            }
         }
-        if (kt + 1 < nk) {
-            step(kt, 0);
-            mfmas(1);
-        } else {
+    } else {
+        // Two waves per SIMD: one register set of fragments; while one wave
+        // waits for its fragment reads the other wave's MFMAs run. Step kt:
+        // wait for slab kt (slabs kt+1 .. kt+STAGES-2 may stay in flight),
+        // barrier (every wave is done with slab kt-1, so its stage is free),
+        // refill that stage with slab kt+STAGES-1, read slab kt, multiply.
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue_loads(s, s * BK);
+        for (int kt = 0; kt < nk; ++kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(STAGES - 2) * T::kLoads>();
+            __syncthreads();
+            issue_loads((kt + STAGES - 1) & (STAGES - 1), (kt + STAGES - 1) * BK);
+            load_frags(0, kt & (STAGES - 1));
             mfmas(0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -279,11 +298,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     }
 }
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, int GROUP_M>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH, int GROUP_M>
 hipError_t launch_bf16(const Problem &p, int64_t grid, hipStream_t stream)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((mmrelu_bf16_mfma<BM, BN, BK, STAGES, WAVES_M, WAVES_N>), dim3(static_cast<uint32_t>(grid)),
+    hipLaunchKernelGGL((mmrelu_bf16_mfma<BM, BN, BK, STAGES, WAVES_M, WAVES_N, PREFETCH>), dim3(static_cast<uint32_t>(grid)),
                        dim3(WAVES_M * WAVES_N * 64), 0, stream, static_cast<const uint16_t *>(p.A),
                        static_cast<const uint16_t *>(p.B), static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda,
                        p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M);
@@ -294,8 +313,14 @@ hipError_t launch_bf16(const Problem &p, int64_t grid, hipStream_t stream)
 
 const Variant *variant_bf16_mfma256()
 {
-    static const Variant v = {"mmrelu_bf16_mfma<256,256,32,4,2,2>", MMRELU_DTYPE_BF16, 256, 256, 32, 256, 1, 8,
-                              launch_bf16<256, 256, 32, 4, 2, 2, 4>};
+    static const Variant v = {"mmrelu_bf16_mfma<256,256,32,4,2,2,prefetch>", MMRELU_DTYPE_BF16, 256, 256, 32, 256, 1, 8,
+                              launch_bf16<256, 256, 32, 4, 2, 2, true, 4>};
+    return &v;
+}
+const Variant *variant_bf16_mfma256_8w()
+{
+    static const Variant v = {"mmrelu_bf16_mfma<256,256,32,4,2,4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
+                              launch_bf16<256, 256, 32, 4, 2, 4, false, 4>};
     return &v;
 }
 

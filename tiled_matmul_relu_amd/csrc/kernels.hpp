@@ -37,5 +37,7 @@ const Variant *variant_bf16_simple();
 const Variant *variant_f32_mfma128();
 const Variant *variant_f32_mfma128_unaligned();
 const Variant *variant_bf16_mfma256();
+const Variant *variant_bf16_mfma256_8w();
+const Variant *variant_bf16_pingpong256();
 
 }  // namespace mmrelu

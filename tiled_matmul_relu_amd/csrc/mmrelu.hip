@@ -16,7 +16,7 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 3;
-constexpr int kNumBf16 = 2;
+constexpr int kNumBf16 = 4;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -25,7 +25,8 @@ const Variant *const *f32_table()
 }
 const Variant *const *bf16_table()
 {
-    static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256()};
+    static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256(),
+                                               variant_bf16_mfma256_8w(), variant_bf16_pingpong256()};
     return t;
 }
 
@@ -100,7 +101,7 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     (void)M;
     if (dtype == MMRELU_DTYPE_F32)
         return layout_fits(f32_table()[1], N, K, lda, ldb, ldc, A, B, C) ? 1 : 2;
-    return layout_fits(bf16_table()[1], N, K, lda, ldb, ldc, A, B, C) ? 1 : 0;
+    return layout_fits(bf16_table()[3], N, K, lda, ldb, ldc, A, B, C) ? 3 : 0;
 }
 
 int fill_plan(const Variant *v, int32_t index, int64_t M, int64_t N, int32_t cus, mmrelu_plan_t *out)
