@@ -12,27 +12,39 @@
 // fp32 accumulation (v_mfma_f32_16x16x32_bf16), ReLU on the accumulator, one
 // rounding to bf16 (nearest, ties to even), one masked store.
 //
-// Layout: wave w belongs to group w / 4; within a group, waves (wm, wn') =
+// Waves: wave w belongs to group w / 4; within a group, (wm, wn') =
 // ((w%4)/2, (w%4)%2) and the wave owns rows 128*wm .. +128 and columns
 // 64*(wn' + 2*group) .. +64 of the tile (8 x 4 MFMA blocks, 128 fp32
-// accumulators per lane). LDS stages, fragment reads, the transposed B reads
-// (ds_read_b64_tr_b16) and the copy layout are those of the four-wave kernel
-// in k_bf16_mfma.hip. Group 0 copies the B half of every slab, group 1 the
-// A half.
+// accumulators per lane). Slabs are 32 deep along K.
 //
-// Schedule (S stages, slabs of 32 along K; interval I_t ends at a barrier):
-//   prologue: every wave copies its half of slabs 0 .. S-2; wait; barrier;
-//             I_-1: group 0 reads slab 0, copies its half of slab S-1.
+// LDS (160 KB): A is staged per PAIR of slabs (64 k, 128 bytes per row) in a
+// ring of three 32 KB stages, B per slab in a ring of four 16 KB stages.
+//  - A stage: row r's 16-byte chunk c sits at r*128 + 16*(c ^ (r%8)). One
+//    copy instruction moves 8 rows x 128 bytes: lane 8r'+j fetches chunk
+//    j ^ r' of its row, so each group of 8 lanes reads one whole 128-byte
+//    line from global memory and writes it, permuted, to one LDS row. (With
+//    32-deep A slabs a row contributes only 64 bytes, and the global reads
+//    touch every line twice.) A fragment reads (16 lanes: 16 rows, one chunk)
+//    hit 16 distinct chunk positions and run at the full LDS rate.
+//  - B stage: 32 rows of 512 bytes, 16-byte chunks XOR-swizzled by row, read
+//    with ds_read_b64_tr_b16 (each lane gets 8 consecutive k of a column).
+// Group 1 copies A, group 0 copies B; every wave issues four 1 KB copies per
+// memory interval.
+//
+// Schedule (interval I_t ends at a barrier):
+//   prologue: group 1 copies A pairs 0 and 1, group 0 B slabs 0..2; wait for
+//             slab 0; barrier. I_-1: group 0 reads slab 0, copies B slab 3.
 //   I_2k:   group 0 multiplies slab k;
-//           group 1 reads slab k, copies its half of slab k+S-1.
-//           Both then wait until slab k+1 has landed (slabs up to k+S-2 may
-//           stay in flight: vmcnt((S-2) * 4)).
-//   I_2k+1: group 0 reads slab k+1, copies its half of slab k+S;
+//           group 1 reads slab k and copies half (k%2) of A pair (k+4)/2.
+//           Both then wait for their copies issued two memory intervals
+//           earlier (vmcnt(8)), which completes slab k+1.
+//   I_2k+1: group 0 reads slab k+1 and copies B slab k+4;
 //           group 1 multiplies slab k.
-// Slab j's stage is refilled (with slab j+S) from I_2j+1 on: by then group 0
-// read it in I_2j-1 and group 1 in I_2j. Copies past K are fully masked and
-// only zero-fill a stage that is never read, so every slab costs the same
-// vmcnt count and the loop has no data-dependent branches.
+// A pair p's stage last held pair p-3, whose second slab group 1 read in
+// I_4p-10; B slab m's stage last held slab m-4, read by group 1 in I_2m-8.
+// Copies past K are fully masked (they zero-fill stages that are never
+// read), so every interval costs the same vmcnt count and the loop has no
+// data-dependent branches.
 //
 // Requires lda, ldb, ldc, K and N to be multiples of 8 and 16-byte aligned
 // pointers.
@@ -47,23 +59,24 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kThreads = 512;
-constexpr int kMB = 8, kNB = 4;                 // MFMA blocks per wave: 128 x 64
-constexpr int kCA = kBK / 8;                    // 16-byte k chunks per A row
-constexpr int kCB = kBN / 8;                    // 16-byte chunks per B row
-constexpr int kStageA = kBM * kBK;              // elements
-constexpr int kStage = kBM * kBK + kBK * kBN;   // elements per stage
-constexpr int kCopies = 4;                      // 1 KB copies per wave per slab
+constexpr int kMB = 8, kNB = 4;                       // MFMA blocks per wave: 128 x 64
+constexpr int kStagesA = 3, kStagesB = 4;
+constexpr int kStageABytes = kBM * 2 * kBK * 2;       // one pair of slabs of A: 32 KB
+constexpr int kStageBBytes = kBK * kBN * 2;           // one slab of B: 16 KB
+constexpr int kBBase = kStagesA * kStageABytes;       // byte offset of the B ring
+constexpr int kLdsBytes = kBBase + kStagesB * kStageBBytes;
+constexpr int kCopies = 4;                            // 1 KB copies per wave per memory interval
+constexpr int kWait = 2 * kCopies;                    // copies a wave may leave in flight at a wait
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int STAGES>
+template <int ORDER>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m)
 {
-    static_assert((STAGES & (STAGES - 1)) == 0 && STAGES >= 3, "power-of-two ring of at least three stages");
-    static_assert(kCopies * STAGES <= 63, "copies in flight must fit the vmcnt counter");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * kStage];
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsBytes / 2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -76,75 +89,100 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const int m0 = tm * kBM, n0 = tn * kBN;
     const uint32_t lds0 = lds_address(lds);
 
-    // Copy plan: copy q of wave wl of a group fills 1 KB block 4q + wl of the
-    // group's half of a stage (group 1: A, 16 rows x 4 k chunks, chunk-major;
-    // group 0: B, two 512-byte rows). Edges in M and N are folded into the
-    // offsets once; B rows past K fall outside the rebased B resource; A
-    // chunks past K are tested per slab.
+    // Copy plans. Group 1, A: copy q of half hh of a pair covers rows
+    // 128hh + 8(4q + wl) .. +8; lane 8r'+j fetches chunk c = j ^ r' (8 k) of
+    // row r'. Rows past M get an out-of-range offset here, chunks past K per
+    // pair. Group 0, B: copy q covers B rows 2(4q + wl) .. +2 of a slab,
+    // lane l chunk (l%32) ^ swz(row); columns past N are masked here, rows
+    // past K fall outside the B resource rebased to the slab.
     const rsrc_t ra = make_rsrc(A + static_cast<int64_t>(m0) * lda, ((static_cast<int64_t>(M) - 1 - m0) * lda + K) * 2);
-    uint32_t voff[kCopies];
-    int a_col[kCopies];
+    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    // (Two separate arrays, selected with ?: below: one array indexed by a
+    // run-time half would be placed in scratch memory.)
+    uint32_t voff0[kCopies], voff1[kCopies];
 #pragma unroll
     for (int q = 0; q < kCopies; ++q) {
-        const int blk = 4 * q + wl;
         if (grp == 1) {
-            const int row = blk * 16 + (lane & 15);
-            const int col = (lane >> 4) * 8;
-            a_col[q] = col;
-            voff[q] = (m0 + row < M) ? static_cast<uint32_t>((row * lda + col) * 2) : kOutOfRange;
+            const int row = 8 * (4 * q + wl) + (lane >> 3);
+            voff0[q] = (m0 + row < M) ? static_cast<uint32_t>((row * lda + 8 * a_chunk) * 2) : kOutOfRange;
+            voff1[q] = (m0 + 128 + row < M) ? static_cast<uint32_t>(((row + 128) * lda + 8 * a_chunk) * 2) : kOutOfRange;
         } else {
-            const int row = blk * 2 + (lane >> 5);
+            const int row = 2 * (4 * q + wl) + (lane >> 5);
             const int col = ((lane & 31) ^ swz_b(row)) * 8;
-            a_col[q] = 0;
-            voff[q] = (n0 + col < N) ? static_cast<uint32_t>((row * ldb + col) * 2) : kOutOfRange;
+            voff0[q] = (n0 + col < N) ? static_cast<uint32_t>((row * ldb + col) * 2) : kOutOfRange;
+            voff1[q] = kOutOfRange;
         }
     }
-    // This wave's half of slab `slab` into its stage.
-    auto copy_half = [&](int slab) __attribute__((always_inline)) {
-        const int k0 = slab * kBK;
-        const uint32_t st = lds0 + (slab & (STAGES - 1)) * (kStage * 2);
-        if (grp == 1) {
-#pragma unroll
-            for (int q = 0; q < kCopies; ++q) {
-                const uint32_t off = (a_col[q] < K - k0) ? voff[q] : kOutOfRange;
-                load_to_lds<16>(ra, st + (4 * q + wl) * 1024, off, static_cast<uint32_t>(k0) * 2);
-            }
-        } else {
-            const rsrc_t rb = make_rsrc(B + static_cast<int64_t>(k0) * ldb + n0,
-                                        ((static_cast<int64_t>(K) - 1 - k0) * ldb + N - n0) * 2);
-#pragma unroll
-            for (int q = 0; q < kCopies; ++q)
-                load_to_lds<16>(rb, st + kStageA * 2 + (4 * q + wl) * 1024, voff[q]);
-        }
+    // Copy q of half hh of A pair p (group 1).
+    auto copy_a = [&](int p, int hh, int q) __attribute__((always_inline)) {
+        const int k0 = 2 * kBK * p;
+        const uint32_t off = (8 * a_chunk < K - k0) ? (hh ? voff1[q] : voff0[q]) : kOutOfRange;
+        const uint32_t st = lds0 + (p % kStagesA) * kStageABytes + (128 * hh + 8 * (4 * q + wl)) * 128;
+        load_to_lds<16>(ra, st, off, static_cast<uint32_t>(k0) * 2);
+    };
+    // Copy q of B slab m (group 0); rb is the B resource rebased to the slab.
+    auto b_rsrc = [&](int m) __attribute__((always_inline)) {
+        const int k0 = m * kBK;
+        return make_rsrc(B + static_cast<int64_t>(k0) * ldb + n0, ((static_cast<int64_t>(K) - 1 - k0) * ldb + N - n0) * 2);
+    };
+    auto copy_b = [&](int m, int q, const rsrc_t &rb) __attribute__((always_inline)) {
+        const uint32_t st = lds0 + kBBase + (m % kStagesB) * kStageBBytes + (4 * q + wl) * 1024;
+        load_to_lds<16>(rb, st, voff0[q]);
     };
 
-    // Fragment read plan (element offsets into a stage), as in the four-wave
-    // kernel: A block i at rows wm*128 + 16i + t, chunk g; B block j at
-    // columns wn*64 + 16j + 4(t%4), rows 8g + t/4 (+4h).
-    const int a_off = ((wm * kMB * kCA + g) * 16 + t) * 8;
+    // Fragment read plan (element offsets). A block i of slab s: rows
+    // wm*128 + 16i + t, chunk 4(s%2) + g of the pair. B block j: columns
+    // wn*64 + 16j + 4(t%4), rows 8g + t/4 (+4h) of the slab.
+    const int a_off0 = (wm * 128 + t) * 64 + ((g ^ (t & 7)) << 3);
+    const int a_off1 = (wm * 128 + t) * 64 + (((4 + g) ^ (t & 7)) << 3);
     int b_off[kNB];
     {
         const int k_lane = 8 * g + (t >> 2);
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
             const int n = wn * 64 + j * 16 + 4 * (t & 3);
-            b_off[j] = kStageA + k_lane * kBN + (((n >> 3) ^ swz_b(k_lane)) << 3) + (n & 7);
+            b_off[j] = kBBase / 2 + k_lane * kBN + (((n >> 3) ^ swz_b(k_lane)) << 3) + (n & 7);
         }
     }
 
+    // Part p of the fragments of slab s: B block p (two transposed reads)
+    // and A blocks 2p, 2p+1.
     bf16x8 fa[kMB], fb[kNB];
-    auto read_frags = [&](int slab) __attribute__((always_inline)) {
-        const uint16_t *st = lds + (slab & (STAGES - 1)) * kStage;
+    auto read_part = [&](int s, int p) __attribute__((always_inline)) {
+        const uint16_t *sa = lds + ((s >> 1) % kStagesA) * (kStageABytes / 2) + ((s & 1) ? a_off1 : a_off0);
+        const uint16_t *sb = lds + (s % kStagesB) * (kStageBBytes / 2);
+        i16x4 half[2];
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) {
-            i16x4 half[2];
+        for (int h = 0; h < 2; ++h)
+            half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(sb + b_off[p] + 4 * h * kBN));
+        fb[p] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(st + b_off[j] + 4 * h * kBN));
-            fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int i = 2 * p; i < 2 * p + 2; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
+    };
+    // The memory role of one interval: read the fragments of slab `rd` (if
+    // `do_read`) and issue this wave's four copies, copy(q). ORDER picks the
+    // instruction order: 0 all reads then all copies, 1 all copies then all
+    // reads, 2 copy/read-part pairs, 3 read-part/copy pairs. (Copies are
+    // volatile asm with a memory clobber, so the order is kept.)
+    auto mem_work = [&](int rd, bool do_read, auto &&copy) __attribute__((always_inline)) {
+        if constexpr (ORDER == 0 || ORDER == 1) {
+            if (ORDER == 0 && do_read)
+#pragma unroll
+                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+#pragma unroll
+            for (int q = 0; q < kCopies; ++q) copy(q);
+            if (ORDER == 1 && do_read)
+#pragma unroll
+                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+        } else {
+            static_assert(kNB == kCopies, "one copy per fragment part");
+#pragma unroll
+            for (int p = 0; p < kNB; ++p) {
+                if (ORDER == 2) copy(p);
+                if (do_read) read_part(rd, p);
+                if (ORDER == 3) copy(p);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(st + a_off + i * 16 * kBK);
     };
 
     f32x4 acc[kMB][kNB];
@@ -163,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     // barriers (MFMAs touch no memory and would otherwise be moved across).
     auto interval_end = [&](bool wait_copies) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        if (wait_copies) wait_vmcnt<(STAGES - 2) * kCopies>();
+        if (wait_copies) wait_vmcnt<kWait>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -172,25 +210,40 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     // the MFMA chain per code path); both execute the same barriers.
     const int nk = (K + kBK - 1) / kBK;
     if (nk > 0) {
+        if (grp == 1) {
 #pragma unroll
-        for (int s = 0; s + 1 < STAGES; ++s) copy_half(s);
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int q = 0; q < kCopies; ++q) copy_a(p, hh, q);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const rsrc_t rb = b_rsrc(m);
+#pragma unroll
+                for (int q = 0; q < kCopies; ++q) copy_b(m, q, rb);
+            }
+        }
         interval_end(true);                          // slab 0 has landed
         if (grp == 0) {
-            read_frags(0);                           // I_-1
-            copy_half(STAGES - 1);
+            {
+                const rsrc_t rb = b_rsrc(3);
+                mem_work(0, true, [&](int q) __attribute__((always_inline)) { copy_b(3, q, rb); });   // I_-1
+            }
             interval_end(false);
             for (int k = 0; k < nk; ++k) {
                 mfmas();                             // I_2k
                 interval_end(true);                  // slab k+1 has landed
-                if (k + 1 < nk) read_frags(k + 1);   // I_2k+1
-                copy_half(k + STAGES);
+                const rsrc_t rb = b_rsrc(k + 4);     // I_2k+1
+                mem_work(k + 1, k + 1 < nk, [&](int q) __attribute__((always_inline)) { copy_b(k + 4, q, rb); });
                 interval_end(false);
             }
         } else {
             interval_end(false);                     // I_-1
             for (int k = 0; k < nk; ++k) {
-                read_frags(k);                       // I_2k
-                copy_half(k + STAGES - 1);
+                const int p = (k + 4) >> 1, hh = k & 1;   // I_2k
+                mem_work(k, true, [&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });
                 interval_end(true);                  // slab k+1 has landed
                 mfmas();                             // I_2k+1
                 interval_end(false);
@@ -219,11 +272,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     }
 }
 
-template <int STAGES, int GROUP_M>
+template <int ORDER, int GROUP_M>
 hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 {
     const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((mmrelu_bf16_pingpong<STAGES>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((mmrelu_bf16_pingpong<ORDER>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
                        static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M);
     return hipGetLastError();
@@ -233,8 +286,8 @@ hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 
 const Variant *variant_bf16_pingpong256()
 {
-    static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_pingpong<4, 4>};
+    static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
+                              launch_pingpong<3, 4>};
     return &v;
 }
 
