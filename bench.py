@@ -53,6 +53,68 @@ def measured_traffic(kind: str, kernel_name: str):
     return rec.get("bytes_per_launch")
 
 
+def read_counters(path, counter):
+    """Per-kernel lists of one counter's per-dispatch values from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def record_traffic(fetch_csv, write_csv, calib_mib, command):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch) that included the
+    calibration copy of calib_mib MiB (--calib-copy-mib). Each counter is scaled
+    by what it reads for that copy, whose true traffic is calib_mib MiB read and
+    calib_mib MiB written."""
+    import datagen
+    import tiled_matmul_relu_amd as mm
+    fetch = read_counters(fetch_csv, "FETCH_SIZE")
+    write = read_counters(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if len(copy) != 1 or copy[0] not in write:
+        raise SystemExit(f"record-traffic: expected one copy kernel in the counter files, found {copy}")
+    calib = calib_mib * (1 << 20)
+    f_fac = calib / (fetch[copy[0]][-1] * 1024)
+    w_fac = calib / (write[copy[0]][-1] * 1024)
+    recs = {}
+    for kind, cid in (("bf16", 5), ("f32", 3)):
+        cfg = datagen.CONFIGS[cid]
+        plan = mm.mmrelu_plan(mm.DTYPE_BF16 if kind == "bf16" else mm.DTYPE_F32, cfg.M, cfg.N, cfg.K,
+                              cfg.lda, cfg.ldb, cfg.ldc)
+        family = plan["name"].split("<")[0]          # the planner's kernel for this workload
+        names = [k for k in fetch if family + "<" in k]
+        if len(names) != 1 or names[0] not in write:
+            raise SystemExit(f"record-traffic: expected one {family} kernel, found {names}")
+        fv, wv = fetch[names[0]], write[names[0]]
+        fb = sum(fv) / len(fv) * 1024 * f_fac
+        wb = sum(wv) / len(wv) * 1024 * w_fac
+        s_in = 2 if kind == "bf16" else 4
+        recs[plan["name"]] = {
+            "kernel_symbol": names[0].split(">(")[0] + ">",
+            "workload": cfg.name,
+            "source_sha256": source_hash(kind),
+            "bytes_per_launch": round(fb + wb),
+            "fetch_bytes_per_launch": round(fb),
+            "write_bytes_per_launch": round(wb),
+            "algorithmic_bytes": s_in * (cfg.M * cfg.K + cfg.K * cfg.N) + s_in * cfg.M * cfg.N,
+            "dispatches": min(len(fv), len(wv)),
+            "fetch_scale": round(f_fac, 4),
+            "write_scale": round(w_fac, 4),
+            "calibration": f"{calib_mib} MiB device-to-device copy in the same run",
+            "command": command,
+        }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(recs, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(recs, indent=1, sort_keys=True))
+
+
 def to_device(x, torch):
     import numpy as np
     if x.dtype == np.uint16:
@@ -108,15 +170,27 @@ def cpu_baseline(cfg, a, b, target_s, oracle):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The first ~25 calls of a fresh process run while clocks and power
+    # management settle (up to 30% slower); the defaults time the sustained rate.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32 4096^3 workload")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of known traffic, "
                          "for scaling memory counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: write profiles/traffic.json from the counter_collection.csv files of "
+                         "two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with --calib-copy-mib")
+    ap.add_argument("--traffic-command", default="", help="the profiling command, stored with --record-traffic")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        if args.calib_copy_mib <= 0:
+            ap.error("--record-traffic needs --calib-copy-mib (the size the profiled runs copied)")
+        record_traffic(args.record_traffic[0], args.record_traffic[1], args.calib_copy_mib, args.traffic_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; relu(A·B) shards by rows or columns of C with no "

@@ -287,7 +287,7 @@ hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 const Variant *variant_bf16_pingpong256()
 {
     static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_pingpong<3, 4>};
+                              launch_pingpong<2, 8>};
     return &v;
 }
 
