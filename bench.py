@@ -13,6 +13,7 @@ baseline (the fp64 oracle timed on a bounded sample of the same workload on
 this host's cores).
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -177,6 +178,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32 4096^3 workload")
+    ap.add_argument("--no-power-check", action="store_true",
+                    help="skip timing the bf16 kernel on all-zero inputs (the power-cap check)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of known traffic, "
                          "for scaling memory counters)")
@@ -232,6 +235,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic},
     }
+    if not args.no_power_check:
+        # Same kernel, same shape, all-zero inputs: the matrix cores see no
+        # operand toggling, so the board's power cap does not lower the clock.
+        # The gap to `value` is the power cost of random operands, not schedule.
+        zero = dataclasses.replace(head, name=head.name + "_zeros", dist="zeros")
+        rz = time_workload(zero, args.steps, args.warmup, torch, mm, datagen)
+        out["power_check"] = {"inputs": "all-zero bf16 A and B, same shape, kernel and launch",
+                              "value": round(rz["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(rz["ms"], 4),
+                              "frac": round(rz["tflops"] / PEAK_TFLOPS["bf16"], 4)}
     if not args.no_f32:
         f = datagen.CONFIGS[3]
         r32 = time_workload(f, args.steps, args.warmup, torch, mm, datagen)

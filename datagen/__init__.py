@@ -132,7 +132,7 @@ class Config:
     lda: int
     ldb: int
     ldc: int
-    dist: str           # "normal_over_sqrtk" or "uniform_pm1"
+    dist: str           # "normal_over_sqrtk", "uniform_pm1", "small_int" or "zeros"
 
     @property
     def seed_a(self) -> int:
@@ -170,6 +170,8 @@ def draw(dist: str, seed: int, rows: int, cols: int, K: int) -> np.ndarray:
         return uniform_pm1_f32(seed, rows, cols)
     if dist == "small_int":
         return small_int_f32(seed, rows, cols)
+    if dist == "zeros":
+        return np.zeros((rows, cols), dtype=np.float32)
     raise ValueError(f"unknown distribution {dist!r}")
 
 

@@ -56,3 +56,8 @@ def test_bf16_bits_roundtrip():
     y = datagen.bf16_bits_to_f32(h)
     assert np.all(np.abs(y - x) <= np.abs(x) * 2.0 ** -8)
     np.testing.assert_array_equal(datagen.f32_to_bf16_bits(y), h)
+
+
+def test_zero_distribution():
+    z = datagen.draw("zeros", 7, 3, 5, 5)
+    assert z.dtype == np.float32 and z.shape == (3, 5) and not z.any()

@@ -196,6 +196,22 @@ def test_k_zero_writes_zeros(dtype):
     assert np.all(c == 0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_inputs_give_zero_outputs(dtype):
+    """All-zero A and B (the inputs of bench.py's power check): every variant
+    writes +0 or -0 everywhere, over several tiles and a ragged tail."""
+    M, N, K = 520, 264, 200
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    a = np.zeros((M, K), np.float32 if dtype == "f32" else np.uint16)
+    b = np.zeros((K, N), a.dtype)
+    for v in variants(kind):
+        if not accepts(kind, v, N, K, K, N, N):
+            continue
+        c, _ = run(a, b, M, N, K, K, N, variant=v)
+        vals = c if dtype == "f32" else datagen.bf16_bits_to_f32(c)
+        assert np.all(vals == 0), f"variant {v}"
+
+
 def test_empty_outputs_launch_nothing():
     t = torch.zeros(4, 4, device="cuda")
     s = torch.cuda.current_stream().cuda_stream

@@ -66,7 +66,6 @@ constexpr int kStageBBytes = kBK * kBN * 2;           // one slab of B: 16 KB
 constexpr int kBBase = kStagesA * kStageABytes;       // byte offset of the B ring
 constexpr int kLdsBytes = kBBase + kStagesB * kStageBBytes;
 constexpr int kCopies = 4;                            // 1 KB copies per wave per memory interval
-constexpr int kWait = 2 * kCopies;                    // copies a wave may leave in flight at a wait
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
@@ -165,7 +164,12 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     // reads, 2 copy/read-part pairs, 3 read-part/copy pairs. (Copies are
     // volatile asm with a memory clobber, so the order is kept.)
     auto mem_work = [&](int rd, bool do_read, auto &&copy) __attribute__((always_inline)) {
-        if constexpr (ORDER == 0 || ORDER == 1) {
+        if constexpr (ORDER == 4) {
+            (void)copy;
+            if (do_read)
+#pragma unroll
+                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+        } else if constexpr (ORDER == 0 || ORDER == 1) {
             if (ORDER == 0 && do_read)
 #pragma unroll
                 for (int p = 0; p < kNB; ++p) read_part(rd, p);
@@ -197,11 +201,29 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
             for (int j = 0; j < kNB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     };
-    // End of an interval. The fences keep each interval's work between its
-    // barriers (MFMAs touch no memory and would otherwise be moved across).
-    auto interval_end = [&](bool wait_copies) __attribute__((always_inline)) {
+    // ORDER 4: the MFMA role issues the copies, one after every 8 MFMAs.
+    auto mfmas_copy = [&](auto &&copy) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            if (i & 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                copy(i >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    auto no_copy = [](int) {};
+    // End of an interval: wait until at most `in_flight` of this wave's
+    // copies are outstanding (if in_flight >= 0), then the barrier. The
+    // fences keep each interval's work between its barriers (MFMAs touch no
+    // memory and would otherwise be moved across).
+    auto interval_end = [&](int in_flight) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        if (wait_copies) wait_vmcnt<kWait>();
+        if (in_flight == 8) wait_vmcnt<8>();
+        if (in_flight == 4) wait_vmcnt<4>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -225,28 +247,45 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                 for (int q = 0; q < kCopies; ++q) copy_b(m, q, rb);
             }
         }
-        interval_end(true);                          // slab 0 has landed
+        interval_end(8);                             // slab 0 has landed
         if (grp == 0) {
-            {
+            if constexpr (ORDER == 4) {
+                mem_work(0, true, no_copy);          // I_-1
+            } else {
                 const rsrc_t rb = b_rsrc(3);
                 mem_work(0, true, [&](int q) __attribute__((always_inline)) { copy_b(3, q, rb); });   // I_-1
             }
-            interval_end(false);
+            interval_end(-1);
             for (int k = 0; k < nk; ++k) {
-                mfmas();                             // I_2k
-                interval_end(true);                  // slab k+1 has landed
-                const rsrc_t rb = b_rsrc(k + 4);     // I_2k+1
-                mem_work(k + 1, k + 1 < nk, [&](int q) __attribute__((always_inline)) { copy_b(k + 4, q, rb); });
-                interval_end(false);
+                if constexpr (ORDER == 4) {          // I_2k (B slab k+3 replaces slab k-1)
+                    const rsrc_t rb = b_rsrc(k + 3);
+                    mfmas_copy([&](int q) __attribute__((always_inline)) { copy_b(k + 3, q, rb); });
+                } else {
+                    mfmas();                         // I_2k
+                }
+                interval_end(8);                     // slab k+1 has landed
+                if constexpr (ORDER == 4) {          // I_2k+1
+                    mem_work(k + 1, k + 1 < nk, no_copy);
+                } else {
+                    const rsrc_t rb = b_rsrc(k + 4);
+                    mem_work(k + 1, k + 1 < nk, [&](int q) __attribute__((always_inline)) { copy_b(k + 4, q, rb); });
+                }
+                interval_end(-1);
             }
         } else {
-            interval_end(false);                     // I_-1
+            interval_end(-1);                        // I_-1
             for (int k = 0; k < nk; ++k) {
-                const int p = (k + 4) >> 1, hh = k & 1;   // I_2k
-                mem_work(k, true, [&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });
-                interval_end(true);                  // slab k+1 has landed
-                mfmas();                             // I_2k+1
-                interval_end(false);
+                const int p = (k + 4) >> 1, hh = k & 1;
+                if constexpr (ORDER == 4) {
+                    mem_work(k, true, no_copy);      // I_2k
+                    interval_end(4);                 // slab k+1 has landed
+                    mfmas_copy([&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k+1
+                } else {
+                    mem_work(k, true, [&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k
+                    interval_end(8);                 // slab k+1 has landed
+                    mfmas();                         // I_2k+1
+                }
+                interval_end(-1);
             }
         }
     }
