@@ -150,6 +150,50 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b)}
 
 
+def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None):
+    """Per-call HIP-event times (ms) of one workload: mean, median, P95, and
+    the rates derived from the median."""
+    a, b = datagen.make_inputs(cfg)
+    da, db = to_device(a, torch), to_device(b, torch)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    c = torch.empty((cfg.M, cfg.ldc), dtype=dt, device="cuda")
+    stream = torch.cuda.current_stream()
+    kind = mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16
+    if variant is None:
+        fn = mm.mmrelu_f32 if cfg.dtype == "f32" else mm.mmrelu_bf16
+        args = ()
+    else:
+        fn = mm.mmrelu_f32_variant if cfg.dtype == "f32" else mm.mmrelu_bf16_variant
+        args = (variant,)
+    args += (da.data_ptr(), db.data_ptr(), c.data_ptr(), cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc,
+             stream.cuda_stream)
+    for _ in range(warmup):
+        rc = fn(*args)
+        if rc != mm.MMRELU_OK:
+            raise RuntimeError(mm.status_string(rc))
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(*args)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mean = sum(t) / steps
+    med = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+    p95 = t[min(steps - 1, int(math.ceil(0.95 * steps)) - 1)]
+    plan = (mm.mmrelu_plan(kind, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc) if variant is None else
+            mm.mmrelu_plan_variant(kind, variant, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc))
+    alg_bytes = cfg.elem_bytes * (cfg.M * cfg.K + cfg.K * cfg.N + cfg.M * cfg.N)
+    tf = cfg.flops / (med * 1e-3) / 1e12
+    return {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K, "lda": cfg.lda, "ldb": cfg.ldb, "ldc": cfg.ldc,
+            "dtype": cfg.dtype, "kernel": plan["name"], "grid": plan["grid"], "waves": plan["waves"],
+            "idle_slots_last_wave": plan["idle_slots_last"], "steps": steps, "warmup": warmup,
+            "mean_ms": round(mean, 5), "median_ms": round(med, 5), "p95_ms": round(p95, 5),
+            "tflops_median": round(tf, 3), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[cfg.dtype], 2),
+            "alg_gbs_median": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(cfg, a, b, target_s, oracle):
     """The oracle timed on rows [0, r) of the workload, r chosen from a short
     calibration run so that the timed part takes about target_s seconds."""
@@ -186,8 +230,24 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: write profiles/traffic.json from the counter_collection.csv files of "
                          "two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with --calib-copy-mib")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the benchmark line: per-call statistics (mean, median, P95, algorithmic GB/s, "
+                         "grid and wave quantization) of all five workloads, one JSON line each")
     ap.add_argument("--traffic-command", default="", help="the profiling command, stored with --record-traffic")
     args = ap.parse_args()
+
+    if args.all_configs:
+        import torch
+        import datagen
+        import tiled_matmul_relu_amd as mm
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        mm.load_library()
+        for ident, cfg in sorted(datagen.CONFIGS.items()):
+            print(json.dumps({"config": ident, **per_call_stats(cfg, args.steps, args.warmup, torch, mm, datagen)}),
+                  flush=True)
+        return
 
     if args.record_traffic:
         if args.calib_copy_mib <= 0:

@@ -98,7 +98,13 @@ typedef struct {
 
 /* Fill *out for a call of this dtype and shape. cus = 0 uses the current
  * device's compute-unit count when a device is present, else 256. Returns a
- * status as above (arguments are validated the same way, pointers aside). */
+ * status as above (arguments are validated the same way, pointers aside).
+ * The choice: among the dtype's matrix-core kernels at a large and a small
+ * tile that accept the layout, the one with the least estimated time on the
+ * busiest compute unit, ceil(tiles / cus) tiles times the tile's outputs
+ * times the kernel's measured relative cost per output; layouts no
+ * matrix-core kernel accepts use the plain tiled kernel (variant 0). The
+ * launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);
 

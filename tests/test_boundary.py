@@ -118,6 +118,34 @@ def test_plans_for_the_workloads():
         mm.mmrelu_plan(7, 4, 4, 4, 4, 4, 4)
 
 
+def test_planner_tile_choice_by_wave_quantization():
+    """Smaller tiles when the large tile's grid leaves CUs idle (the a7 rule:
+    ceil(tiles / CUs) * tile outputs * measured relative cost)."""
+    sq = lambda dt, n, cus=256: mm.mmrelu_plan(dt, n, n, n, n, n, n, cus=cus)
+    # fp32: 256^3 and 1024^3 fit one 64x64 tile per CU; 4096^3 fills the CUs with 128x128
+    for n, tile in ((256, 64), (1024, 64), (4096, 128)):
+        p = sq(mm.DTYPE_F32, n)
+        assert (p["block_m"], p["block_n"]) == (tile, tile) and "unaligned" not in p["name"], (n, p["name"])
+    # the ragged shape: 792 tiles of 128x128 (4 on the busiest CU, 4 * 16384 outputs)
+    # against 3055 of 64x64 (12 on the busiest CU, 12 * 4096 * 1.02)
+    p = mm.mmrelu_plan(mm.DTYPE_F32, 4097, 3001, 2049, 2049, 3001, 3001, cus=256)
+    assert "unaligned" in p["name"] and p["block_m"] == 64 and p["grid"] == 65 * 47
+    # bf16: 128x128 while the 256x256 grid has at most one tile per CU and the
+    # small grid too (1024^2, 2048^2); 256x256 from 3072^2 on
+    for n, tile in ((1024, 128), (2048, 128), (3072, 256), (4096, 256), (6144, 256), (8192, 256)):
+        p = sq(mm.DTYPE_BF16, n)
+        assert p["block_m"] == tile, (n, p["name"])
+    assert "pingpong" in sq(mm.DTYPE_BF16, 8192)["name"]
+    # fewer CUs shift the crossover: on 64 CUs 2048^2 bf16 has one 256x256 tile per CU
+    assert sq(mm.DTYPE_BF16, 2048, cus=64)["block_m"] == 256
+    # the plan's kernel is the one the launch uses: planning with any CU count
+    # stays within the candidates that accept the layout
+    p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1000, 1000, 1000, 1000, 1000, cus=256)
+    assert "mfma" in p["name"] or "pingpong" in p["name"]
+    p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1001, 1000, 1000, 1001, 1001, cus=256)
+    assert "simple" in p["name"]
+
+
 def test_every_variant_plans():
     for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
         n = mm.mmrelu_num_variants(dt)

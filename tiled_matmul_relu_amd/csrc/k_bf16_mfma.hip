@@ -324,4 +324,13 @@ const Variant *variant_bf16_mfma256_8w()
     return &v;
 }
 
+// 128 x 128 tiles (2 x 2 waves of 64 x 64): four times the workgroups of the
+// 256 x 256 tile, for shapes whose 256 x 256 grid leaves most CUs idle.
+const Variant *variant_bf16_mfma128()
+{
+    static const Variant v = {"mmrelu_bf16_mfma<128,128,32,4,2,2,prefetch>", MMRELU_DTYPE_BF16, 128, 128, 32, 256, 2, 8,
+                              launch_bf16<128, 128, 32, 4, 2, 2, true, 8>, 1.55f};
+    return &v;
+}
+
 }  // namespace mmrelu

@@ -260,4 +260,19 @@ const Variant *variant_f32_mfma128_unaligned()
     return &v;
 }
 
+// 64 x 64 tiles (2 x 2 waves of 32 x 32): four times the workgroups of the
+// 128 x 128 tile, for shapes whose 128 x 128 grid leaves most CUs idle.
+const Variant *variant_f32_mfma64()
+{
+    static const Variant v = {"mmrelu_f32_mfma<64,64,32,2,2,aligned>", MMRELU_DTYPE_F32, 64, 64, 32, 256, 5, 4,
+                              launch_f32<64, 64, 32, 2, 2, true, 8>, 1.02f};
+    return &v;
+}
+const Variant *variant_f32_mfma64_unaligned()
+{
+    static const Variant v = {"mmrelu_f32_mfma<64,64,32,2,2,unaligned>", MMRELU_DTYPE_F32, 64, 64, 32, 256, 5, 0,
+                              launch_f32<64, 64, 32, 2, 2, false, 8>, 1.02f};
+    return &v;
+}
+
 }  // namespace mmrelu

@@ -28,6 +28,9 @@ struct Variant {
     int align_elems;      // 0: any layout; else lda, ldb, ldc, K, N must be
                           // multiples of this and A, B, C 16-byte aligned
     Launcher launch;
+    // Measured time per output element of a full tile, relative to the
+    // dtype's fastest kernel (the planner's cost model).
+    float rel_cost = 1.0f;
 };
 
 // Kernel variants, defined in the kernel translation units (host functions
@@ -36,8 +39,11 @@ const Variant *variant_f32_simple();
 const Variant *variant_bf16_simple();
 const Variant *variant_f32_mfma128();
 const Variant *variant_f32_mfma128_unaligned();
+const Variant *variant_f32_mfma64();
+const Variant *variant_f32_mfma64_unaligned();
 const Variant *variant_bf16_mfma256();
 const Variant *variant_bf16_mfma256_8w();
 const Variant *variant_bf16_pingpong256();
+const Variant *variant_bf16_mfma128();
 
 }  // namespace mmrelu

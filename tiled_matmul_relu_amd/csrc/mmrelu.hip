@@ -15,18 +15,20 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 3;
-constexpr int kNumBf16 = 4;
+constexpr int kNumF32 = 5;
+constexpr int kNumBf16 = 5;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
-                                              variant_f32_mfma128_unaligned()};
+                                              variant_f32_mfma128_unaligned(), variant_f32_mfma64(),
+                                              variant_f32_mfma64_unaligned()};
     return t;
 }
 const Variant *const *bf16_table()
 {
     static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256(),
-                                               variant_bf16_mfma256_8w(), variant_bf16_pingpong256()};
+                                               variant_bf16_mfma256_8w(), variant_bf16_pingpong256(),
+                                               variant_bf16_mfma128()};
     return t;
 }
 
@@ -93,15 +95,37 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
     return al16(A) && al16(B) && al16(C);
 }
 
-// Planner: the default variant for a dtype and shape. Pointers are taken as
-// 16-byte aligned when null (planning without buffers).
+// Planner: the default variant for a dtype and shape. Candidates are the
+// dtype's matrix-core kernels at two tile sizes that accept the layout; the
+// pick minimises the estimated time of the busiest CU, ceil(tiles / CUs)
+// full tiles of block_m x block_n outputs at the variant's measured relative
+// cost per output (wave quantisation of the grid over the CUs). Layouts no
+// matrix-core kernel accepts go to the plain tiled kernel (variant 0).
+// Pointers are taken as 16-byte aligned when null (planning without buffers).
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                       const void *A, const void *B, const void *C)
+                       const void *A, const void *B, const void *C, int32_t cus)
 {
-    (void)M;
-    if (dtype == MMRELU_DTYPE_F32)
-        return layout_fits(f32_table()[1], N, K, lda, ldb, ldc, A, B, C) ? 1 : 2;
-    return layout_fits(bf16_table()[3], N, K, lda, ldb, ldc, A, B, C) ? 3 : 0;
+    static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {3, 4};
+    const Variant *const *table = dtype == MMRELU_DTYPE_F32 ? f32_table() : bf16_table();
+    const bool fits = layout_fits(table[dtype == MMRELU_DTYPE_F32 ? 1 : 3], N, K, lda, ldb, ldc, A, B, C);
+    const int32_t *cand = nullptr;
+    if (dtype == MMRELU_DTYPE_F32) cand = fits ? f32_aligned : f32_any;
+    else if (fits) cand = bf16_aligned;
+    else return 0;
+    int32_t best = cand[0];
+    double best_cost = 0.0;
+    for (int c = 0; c < 2; ++c) {
+        const Variant *v = table[cand[c]];
+        if (!layout_fits(v, N, K, lda, ldb, ldc, A, B, C)) continue;
+        const int64_t tiles = ((M + v->block_m - 1) / v->block_m) * ((N + v->block_n - 1) / v->block_n);
+        const int64_t per_cu = (tiles + cus - 1) / cus;
+        const double cost = static_cast<double>(per_cu) * v->block_m * v->block_n * v->rel_cost;
+        if (c == 0 || cost < best_cost) {
+            best = cand[c];
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 int fill_plan(const Variant *v, int32_t index, int64_t M, int64_t N, int32_t cus, mmrelu_plan_t *out)
@@ -137,7 +161,7 @@ int run(int dtype, int32_t variant, const void *A, const void *B, void *C, int64
     if (rc != MMRELU_OK) return rc;
     rc = check_pointers(A, B, C, M, N, K, esize);
     if (rc != MMRELU_OK) return rc;
-    if (variant < 0) variant = choose_variant(dtype, M, N, K, lda, ldb, ldc, A, B, C);
+    if (variant < 0) variant = choose_variant(dtype, M, N, K, lda, ldb, ldc, A, B, C, device_cus());
     const Variant *v = variant_at(dtype, variant);
     if (v == nullptr) return MMRELU_ERR_INVALID_VALUE;
     if (K > 0 && !layout_fits(v, N, K, lda, ldb, ldc, A, B, C)) return MMRELU_ERR_INVALID_VALUE;
@@ -230,8 +254,10 @@ int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     if (dtype != MMRELU_DTYPE_F32 && dtype != MMRELU_DTYPE_BF16) return MMRELU_ERR_INVALID_VALUE;
     int rc = check_shape(M, N, K, lda, ldb, ldc);
     if (rc != MMRELU_OK) return rc;
-    return mmrelu_plan_variant(dtype, choose_variant(dtype, M, N, K, lda, ldb, ldc, nullptr, nullptr, nullptr), M,
-                               N, K, lda, ldb, ldc, cus, out);
+    if (cus < 0) return MMRELU_ERR_INVALID_VALUE;
+    const int32_t n_cus = cus > 0 ? cus : device_cus();
+    return mmrelu_plan_variant(dtype, choose_variant(dtype, M, N, K, lda, ldb, ldc, nullptr, nullptr, nullptr, n_cus),
+                               M, N, K, lda, ldb, ldc, n_cus, out);
 }
 
 }  // extern "C"
