@@ -150,23 +150,29 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b)}
 
 
-def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None):
+def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="relu", bias=False):
     """Per-call HIP-event times (ms) of one workload: mean, median, P95, and
-    the rates derived from the median."""
+    the rates derived from the median. act/bias select the fused epilogue
+    (the default is relu(A·B))."""
     a, b = datagen.make_inputs(cfg)
     da, db = to_device(a, torch), to_device(b, torch)
+    dbias = None
+    if bias:
+        bv = datagen.normal_f32(cfg.seed_b + 7, 1, cfg.N, 0.5).ravel()
+        dbias = to_device(datagen.f32_to_bf16_bits(bv) if cfg.dtype == "bf16" else bv, torch)
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     c = torch.empty((cfg.M, cfg.ldc), dtype=dt, device="cuda")
     stream = torch.cuda.current_stream()
     kind = mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16
+    code = {"relu": mm.ACT_RELU, "gelu_tanh": mm.ACT_GELU_TANH, "none": mm.ACT_NONE}[act]
     if variant is None:
-        fn = mm.mmrelu_f32 if cfg.dtype == "f32" else mm.mmrelu_bf16
-        args = ()
+        fn = mm.mmrelu_fused_f32 if cfg.dtype == "f32" else mm.mmrelu_fused_bf16
+        args = (code,)
     else:
-        fn = mm.mmrelu_f32_variant if cfg.dtype == "f32" else mm.mmrelu_bf16_variant
-        args = (variant,)
-    args += (da.data_ptr(), db.data_ptr(), c.data_ptr(), cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc,
-             stream.cuda_stream)
+        fn = mm.mmrelu_fused_f32_variant if cfg.dtype == "f32" else mm.mmrelu_fused_bf16_variant
+        args = (variant, code)
+    args += (da.data_ptr(), db.data_ptr(), dbias.data_ptr() if dbias is not None else 0, c.data_ptr(),
+             cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc, stream.cuda_stream)
     for _ in range(warmup):
         rc = fn(*args)
         if rc != mm.MMRELU_OK:
@@ -186,7 +192,7 @@ def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None):
             mm.mmrelu_plan_variant(kind, variant, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc))
     alg_bytes = cfg.elem_bytes * (cfg.M * cfg.K + cfg.K * cfg.N + cfg.M * cfg.N)
     tf = cfg.flops / (med * 1e-3) / 1e12
-    return {"workload": cfg.name, "M": cfg.M, "N": cfg.N, "K": cfg.K, "lda": cfg.lda, "ldb": cfg.ldb, "ldc": cfg.ldc,
+    return {"workload": cfg.name, "act": act, "bias": bool(bias), "M": cfg.M, "N": cfg.N, "K": cfg.K, "lda": cfg.lda, "ldb": cfg.ldb, "ldc": cfg.ldc,
             "dtype": cfg.dtype, "kernel": plan["name"], "grid": plan["grid"], "waves": plan["waves"],
             "idle_slots_last_wave": plan["idle_slots_last"], "steps": steps, "warmup": warmup,
             "mean_ms": round(mean, 5), "median_ms": round(med, 5), "p95_ms": round(p95, 5),
@@ -233,6 +239,9 @@ def main():
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: per-call statistics (mean, median, P95, algorithmic GB/s, "
                          "grid and wave quantization) of all five workloads, one JSON line each")
+    ap.add_argument("--act", choices=["relu", "gelu_tanh", "none"], default="relu",
+                    help="with --all-configs: the fused epilogue's activation")
+    ap.add_argument("--bias", action="store_true", help="with --all-configs: add a per-column bias")
     ap.add_argument("--traffic-command", default="", help="the profiling command, stored with --record-traffic")
     args = ap.parse_args()
 
@@ -245,8 +254,8 @@ def main():
             sys.exit(1)
         mm.load_library()
         for ident, cfg in sorted(datagen.CONFIGS.items()):
-            print(json.dumps({"config": ident, **per_call_stats(cfg, args.steps, args.warmup, torch, mm, datagen)}),
-                  flush=True)
+            print(json.dumps({"config": ident, **per_call_stats(cfg, args.steps, args.warmup, torch, mm, datagen,
+                                                                act=args.act, bias=args.bias)}), flush=True)
         return
 
     if args.record_traffic:

@@ -71,6 +71,33 @@ int mmrelu_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
                 int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, void *stream);
 
+/*
+ * Fused epilogues (widening of the operation above). The lecture notes make
+ * the point that, with the output tile already in registers before its one
+ * store, any elementwise activation costs nothing extra (section "Reductions
+ * and tiling", the matmul's fusion bonus), and open with GeLU in its tanh form
+ * (section "GeLU three ways: the case for fusion"); a linear layer is a
+ * matmul followed by an activation. For 0 <= i < M, 0 <= j < N:
+ *     C[i][j] = act(sum_{k<K} A[i][k] * B[k][j] + bias[j])
+ * with the sum and the bias added in fp32 and
+ *     MMRELU_ACT_RELU       act(x) = max(x, 0)        (mmrelu_f32 / _bf16)
+ *     MMRELU_ACT_GELU_TANH  act(x) = 0.5 x (1 + tanh(0.79788456 (x + 0.044715 x^3)))
+ *     MMRELU_ACT_NONE       act(x) = x
+ * bias: N elements of the input dtype (fp32, or bf16 bit patterns widened to
+ * fp32), one per output column, or NULL for none; device pointer, caller-owned,
+ * aligned to its element size. bf16 outputs are rounded once, after act.
+ * Errors as above, plus MMRELU_ERR_INVALID_VALUE for an unknown act and
+ * MMRELU_ERR_MISALIGNED for a misaligned bias.
+ */
+enum { MMRELU_ACT_RELU = 0, MMRELU_ACT_GELU_TANH = 1, MMRELU_ACT_NONE = 2 };
+
+int mmrelu_fused_f32(int act, const float *A, const float *B, const float *bias, float *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+int mmrelu_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, uint16_t *C,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
 /* Static text for a status code ("unknown status" for anything else). */
 const char *mmrelu_status_string(int status);
 
@@ -128,6 +155,15 @@ int mmrelu_f32_variant(int32_t variant, const float *A, const float *B, float *C
 int mmrelu_bf16_variant(int32_t variant, const uint16_t *A, const uint16_t *B, uint16_t *C,
                         int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+
+/* The fused entry points with an explicit kernel variant (every variant
+ * applies every epilogue). */
+int mmrelu_fused_f32_variant(int32_t variant, int act, const float *A, const float *B, const float *bias,
+                             float *C, int64_t M, int64_t N, int64_t K,
+                             int64_t lda, int64_t ldb, int64_t ldc, void *stream);
+int mmrelu_fused_bf16_variant(int32_t variant, int act, const uint16_t *A, const uint16_t *B,
+                              const uint16_t *bias, uint16_t *C, int64_t M, int64_t N, int64_t K,
+                              int64_t lda, int64_t ldb, int64_t ldc, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,8 +6,10 @@ shares no code with it; this package does not import the library either.
 
 The arithmetic lives in ``mmrelu_oracle.c`` (plain C, OpenMP over rows),
 built with gcc into ``liboracle.so`` next to it. Each routine is the plain
-definition R[i][j] = max(0, sum_k A[i][k]·B[k][j]) in fp64 with ascending k;
-see the C file for the passages it follows.
+definition R[i][j] = max(0, sum_k A[i][k]·B[k][j]) in fp64 with ascending k,
+and its fused-epilogue form R[i][j] = act(sum_k A[i][k]·B[k][j] + bias[j])
+with act one of ReLU, GeLU (tanh form) or none; see the C file for the
+passages it follows.
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ def build() -> str:
     """Compile liboracle.so with gcc (no fast-math: IEEE double semantics)."""
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
-           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp]
+           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
@@ -48,6 +50,14 @@ def _load():
     for name in ("oracle_mmrelu_f32_at", "oracle_mmrelu_bf16_at"):
         fn = getattr(lib, name)
         fn.argtypes = [p, p, i64, i64, i64, p, p, i64, p]
+        fn.restype = None
+    for name in ("oracle_fused_f32", "oracle_fused_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, i64, i64, i64, i64]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_fused_f32_at", "oracle_fused_bf16_at"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, p, p, i64, p]
         fn.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -116,5 +126,61 @@ def mmrelu_at(a: np.ndarray, b: np.ndarray, rows, cols, K: int, lda: int, ldb: i
     out = np.empty(ii.size, dtype=np.float64)
     if ii.size:
         getattr(_load(), at)(a.ctypes.data, b.ctypes.data, K, lda, ldb,
+                             ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
+    return out
+
+
+ACTS = {"relu": 0, "gelu_tanh": 1, "none": 2}
+
+
+def _bias_ptr(bias, dtype, N):
+    if bias is None:
+        return None
+    if bias.dtype != dtype or not bias.flags.c_contiguous or bias.size < N:
+        raise ValueError("bias must be a C-contiguous array of N elements of the inputs' dtype")
+    return bias.ctypes.data
+
+
+def fused(act: str, a: np.ndarray, b: np.ndarray, bias=None, M=None, N=None, K=None, lda=None,
+          ldb=None) -> np.ndarray:
+    """act(A·B + bias) as an M x N float64 array; ``act`` in ACTS, ``bias``
+    None or N values of the inputs' dtype (float32 or uint16 bf16 patterns)."""
+    dtype, _, _ = _dtype_and_fns(a)
+    if M is None:
+        M, lda = a.shape[0], a.shape[1]
+        K = K if K is not None else a.shape[1]
+        ldb = b.shape[1]
+        N = N if N is not None else b.shape[1]
+    lda = lda if lda is not None else K
+    ldb = ldb if ldb is not None else N
+    _check(a, b, M, N, K, lda, ldb, dtype)
+    bp = _bias_ptr(bias, dtype, N)
+    r = np.empty((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return r
+    fn = "oracle_fused_f32" if dtype == np.float32 else "oracle_fused_bf16"
+    rc = getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, r.ctypes.data, M, N, K, lda, ldb, N)
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its row accumulator")
+    return r
+
+
+def fused_at(act: str, a: np.ndarray, b: np.ndarray, bias, rows, cols, K: int, lda: int, ldb: int) -> np.ndarray:
+    """act(A·B + bias)[rows[t], cols[t]] for each t, as float64."""
+    dtype, _, _ = _dtype_and_fns(a)
+    ii = np.ascontiguousarray(rows, dtype=np.int64)
+    jj = np.ascontiguousarray(cols, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("rows and cols differ in length")
+    if ii.size and (ii.min() < 0 or jj.min() < 0):
+        raise ValueError("negative index")
+    if ii.size and K > 0:
+        if a.size < ii.max() * lda + K or b.size < (K - 1) * ldb + jj.max() + 1:
+            raise ValueError("index beyond the buffers")
+    bp = _bias_ptr(bias, dtype, int(jj.max()) + 1 if jj.size else 0)
+    out = np.empty(ii.size, dtype=np.float64)
+    if ii.size:
+        fn = "oracle_fused_f32_at" if dtype == np.float32 else "oracle_fused_bf16_at"
+        getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, K, lda, ldb,
                              ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
     return out

@@ -34,7 +34,21 @@
  * The sign of a zero result and NaN inputs are outside what the pages fix:
  * s <= 0 (including -0.0) gives +0.0, and a NaN sum gives 0 (parity
  * unpinned for NaN and infinities; the workloads never produce them).
+ *
+ * Fused epilogues (the "oracle_fused_*" routines; the relu routines are the
+ * case act = ReLU without a bias). The lecture applies any elementwise
+ * activation to the finished tile before its one store (section
+ * "Reductions and tiling", the fusion bonus) and defines GeLU by its tanh
+ * form (section "GeLU three ways: the case for fusion"):
+ *
+ *     s' = s + bias[j]           (bias optional, widened exactly to double)
+ *     R  = act(s'), act one of   relu(x)  = x > 0 ? x : 0
+ *                                gelu(x)  = 0.5 x (1 + tanh(0.79788456 (x + 0.044715 x^3)))
+ *                                none(x)  = x
+ *
+ * with the pages' constants and libm's tanh, all in double.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -43,6 +57,19 @@
 #endif
 
 static double relu(double s) { return s > 0.0 ? s : 0.0; }
+
+static double gelu_tanh(double x)
+{
+    return 0.5 * x * (1.0 + tanh(0.79788456 * (x + 0.044715 * x * x * x)));
+}
+
+/* Activation codes: 0 ReLU, 1 GeLU (tanh form), 2 none. */
+static double activate(int act, double s)
+{
+    if (act == 0) return relu(s);
+    if (act == 1) return gelu_tanh(s);
+    return s;
+}
 
 static double widen_bf16(uint16_t h)
 {
@@ -61,11 +88,11 @@ int oracle_num_threads(void)
 #endif
 }
 
-/* Full relu(A·B) for fp32 inputs into a double M x N matrix R (ld ldr).
- * Returns 0, or -1 if a row accumulator could not be allocated. */
-int oracle_mmrelu_f32(const float *A, const float *B, double *R,
-                      int64_t M, int64_t N, int64_t K,
-                      int64_t lda, int64_t ldb, int64_t ldr)
+/* Full act(A·B + bias) for fp32 inputs into a double M x N matrix R (ld
+ * ldr); bias is N floats or NULL. Returns 0, or -1 if a row accumulator
+ * could not be allocated. */
+int oracle_fused_f32(int act, const float *A, const float *B, const float *bias, double *R,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
 {
     int failed = 0;
 #pragma omp parallel
@@ -84,17 +111,17 @@ int oracle_mmrelu_f32(const float *A, const float *B, double *R,
                 const float *brow = B + k * ldb;
                 for (int64_t j = 0; j < N; ++j) acc[j] += a * (double)brow[j];
             }
-            for (int64_t j = 0; j < N; ++j) R[i * ldr + j] = relu(acc[j]);
+            for (int64_t j = 0; j < N; ++j)
+                R[i * ldr + j] = activate(act, acc[j] + (bias ? (double)bias[j] : 0.0));
         }
         free(acc);
     }
     return failed ? -1 : 0;
 }
 
-/* Same for bf16 inputs given as uint16 bit patterns. */
-int oracle_mmrelu_bf16(const uint16_t *A, const uint16_t *B, double *R,
-                       int64_t M, int64_t N, int64_t K,
-                       int64_t lda, int64_t ldb, int64_t ldr)
+/* Same for bf16 inputs and bias given as uint16 bit patterns. */
+int oracle_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, double *R,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
 {
     int failed = 0;
 #pragma omp parallel
@@ -113,7 +140,8 @@ int oracle_mmrelu_bf16(const uint16_t *A, const uint16_t *B, double *R,
                 const uint16_t *brow = B + k * ldb;
                 for (int64_t j = 0; j < N; ++j) acc[j] += a * widen_bf16(brow[j]);
             }
-            for (int64_t j = 0; j < N; ++j) R[i * ldr + j] = relu(acc[j]);
+            for (int64_t j = 0; j < N; ++j)
+                R[i * ldr + j] = activate(act, acc[j] + (bias ? widen_bf16(bias[j]) : 0.0));
         }
         free(acc);
     }
@@ -121,7 +149,20 @@ int oracle_mmrelu_bf16(const uint16_t *A, const uint16_t *B, double *R,
 }
 
 /* Entries R[ii[t]][jj[t]] for t < n, each as one dot product in ascending k. */
-void oracle_mmrelu_f32_at(const float *A, const float *B, int64_t K,
+void oracle_fused_f32_at(int act, const float *A, const float *B, const float *bias, int64_t K,
+                         int64_t lda, int64_t ldb,
+                         const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (double)A[ii[t] * lda + k] * (double)B[k * ldb + jj[t]];
+        out[t] = activate(act, s + (bias ? (double)bias[jj[t]] : 0.0));
+    }
+}
+
+void oracle_fused_bf16_at(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, int64_t K,
                           int64_t lda, int64_t ldb,
                           const int64_t *ii, const int64_t *jj, int64_t n, double *out)
 {
@@ -129,20 +170,36 @@ void oracle_mmrelu_f32_at(const float *A, const float *B, int64_t K,
     for (int64_t t = 0; t < n; ++t) {
         double s = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            s += (double)A[ii[t] * lda + k] * (double)B[k * ldb + jj[t]];
-        out[t] = relu(s);
+            s += widen_bf16(A[ii[t] * lda + k]) * widen_bf16(B[k * ldb + jj[t]]);
+        out[t] = activate(act, s + (bias ? widen_bf16(bias[jj[t]]) : 0.0));
     }
+}
+
+/* relu(A·B): the fused routines with ReLU and no bias. */
+int oracle_mmrelu_f32(const float *A, const float *B, double *R,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldr)
+{
+    return oracle_fused_f32(0, A, B, NULL, R, M, N, K, lda, ldb, ldr);
+}
+
+int oracle_mmrelu_bf16(const uint16_t *A, const uint16_t *B, double *R,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldr)
+{
+    return oracle_fused_bf16(0, A, B, NULL, R, M, N, K, lda, ldb, ldr);
+}
+
+void oracle_mmrelu_f32_at(const float *A, const float *B, int64_t K,
+                          int64_t lda, int64_t ldb,
+                          const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+    oracle_fused_f32_at(0, A, B, NULL, K, lda, ldb, ii, jj, n, out);
 }
 
 void oracle_mmrelu_bf16_at(const uint16_t *A, const uint16_t *B, int64_t K,
                            int64_t lda, int64_t ldb,
                            const int64_t *ii, const int64_t *jj, int64_t n, double *out)
 {
-#pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < n; ++t) {
-        double s = 0.0;
-        for (int64_t k = 0; k < K; ++k)
-            s += widen_bf16(A[ii[t] * lda + k]) * widen_bf16(B[k * ldb + jj[t]]);
-        out[t] = relu(s);
-    }
+    oracle_fused_bf16_at(0, A, B, NULL, K, lda, ldb, ii, jj, n, out);
 }

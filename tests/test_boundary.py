@@ -72,6 +72,29 @@ def test_fp32_alignment_only_needs_4_bytes_bf16_2_bytes():
     assert mm.mmrelu_bf16(A + 2, B, C, 4, 0, 4, 4, 1, 1) == mm.MMRELU_OK
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_entry_points_validate(dtype):
+    E = mm
+    fused = mm.mmrelu_fused_f32 if dtype == "f32" else mm.mmrelu_fused_bf16
+    fused_v = mm.mmrelu_fused_f32_variant if dtype == "f32" else mm.mmrelu_fused_bf16_variant
+    esize = 4 if dtype == "f32" else 2
+    bias = 0x400000
+    # unknown activation codes
+    for act in (-1, 3, 99):
+        assert fused(act, A, B, bias, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+        assert fused_v(0, act, A, B, bias, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    # a bias not aligned to its element size
+    assert fused(E.ACT_GELU_TANH, A, B, bias + esize // 2, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_MISALIGNED
+    # the shape checks apply as in the plain entry points
+    assert fused(E.ACT_NONE, A, B, bias, C, -1, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fused(E.ACT_RELU, A, B, 0, 0, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_NULL_POINTER
+    assert fused_v(-1, E.ACT_RELU, A, B, bias, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    assert fused_v(99, E.ACT_RELU, A, B, bias, C, 4, 4, 4, 4, 4, 4) == E.MMRELU_ERR_INVALID_VALUE
+    # empty outputs launch nothing, with or without a bias
+    assert fused(E.ACT_GELU_TANH, A, B, bias, C, 0, 4, 4, 4, 4, 4) == E.MMRELU_OK
+    assert fused(E.ACT_GELU_TANH, A, B, 0, C, 4, 0, 4, 4, 4, 4) == E.MMRELU_OK
+
+
 def test_variant_entry_points_validate():
     assert mm.mmrelu_f32_variant(-1, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
     assert mm.mmrelu_f32_variant(99, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE

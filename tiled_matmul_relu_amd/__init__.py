@@ -1,4 +1,5 @@
-"""Python binding of libmmrelu, the gfx950 library computing C = relu(A·B).
+"""Python binding of libmmrelu, the gfx950 library computing C = relu(A·B)
+(and its fused-epilogue widening C = act(A·B + bias)).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libmmrelu.so`` (built from ``csrc/`` by ``build.py``). The C
@@ -26,11 +27,16 @@ MMRELU_ERR_MISALIGNED = 3
 MMRELU_ERR_LAUNCH = 4
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+ACT_RELU = 0
+ACT_GELU_TANH = 1
+ACT_NONE = 2
+_ACTS = {"relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH, "none": ACT_NONE}
 
 EXPORTED = (
     "mmrelu_f32", "mmrelu_bf16", "mmrelu_status_string", "mmrelu_version",
     "mmrelu_plan", "mmrelu_num_variants", "mmrelu_plan_variant",
     "mmrelu_wave_quantization", "mmrelu_f32_variant", "mmrelu_bf16_variant",
+    "mmrelu_fused_f32", "mmrelu_fused_bf16", "mmrelu_fused_f32_variant", "mmrelu_fused_bf16_variant",
 )
 
 
@@ -75,6 +81,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for name in ("mmrelu_f32_variant", "mmrelu_bf16_variant"):
         fn = getattr(lib, name)
         fn.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    for name in ("mmrelu_fused_f32", "mmrelu_fused_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    for name in ("mmrelu_fused_f32_variant", "mmrelu_fused_bf16_variant"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
         fn.restype = ctypes.c_int
     lib.mmrelu_status_string.argtypes = [ctypes.c_int]
     lib.mmrelu_status_string.restype = ctypes.c_char_p
@@ -129,6 +143,30 @@ def mmrelu_bf16_variant(variant: int, A: int, B: int, C: int, M: int, N: int, K:
     return load_library().mmrelu_bf16_variant(variant, A, B, C, M, N, K, lda, ldb, ldc, stream)
 
 
+def mmrelu_fused_f32(act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                     ldc: int, stream: int = 0) -> int:
+    """Enqueue C = act(A·B + bias), fp32 (bias: device address of N floats, or 0 for none)."""
+    return load_library().mmrelu_fused_f32(act, A, B, bias or None, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_fused_bf16(act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int, lda: int, ldb: int,
+                      ldc: int, stream: int = 0) -> int:
+    """Enqueue C = act(A·B + bias), bf16 in/out (bias: N bf16 values, or 0), fp32 accumulation."""
+    return load_library().mmrelu_fused_bf16(act, A, B, bias or None, C, M, N, K, lda, ldb, ldc, stream)
+
+
+def mmrelu_fused_f32_variant(variant: int, act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int,
+                             lda: int, ldb: int, ldc: int, stream: int = 0) -> int:
+    return load_library().mmrelu_fused_f32_variant(variant, act, A, B, bias or None, C, M, N, K, lda, ldb, ldc,
+                                                   stream)
+
+
+def mmrelu_fused_bf16_variant(variant: int, act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int,
+                              lda: int, ldb: int, ldc: int, stream: int = 0) -> int:
+    return load_library().mmrelu_fused_bf16_variant(variant, act, A, B, bias or None, C, M, N, K, lda, ldb, ldc,
+                                                    stream)
+
+
 def mmrelu_plan(dtype: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, cus: int = 0) -> dict:
     p = Plan()
     _check(load_library().mmrelu_plan(dtype, M, N, K, lda, ldb, ldc, cus, ctypes.byref(p)), "mmrelu_plan")
@@ -162,12 +200,15 @@ def _ld(t) -> int:
     return max(t.stride(0), t.shape[1], 1)
 
 
-def mmrelu(a, b, out=None, variant: int | None = None, stream=None):
-    """relu(a @ b) for torch device tensors (float32 or bfloat16, row-major).
+def mmrelu(a, b, out=None, variant: int | None = None, stream=None, bias=None, act: str = "relu"):
+    """act(a @ b + bias) for torch device tensors (float32 or bfloat16,
+    row-major); the default is relu(a @ b).
 
-    ``out`` may be a preallocated (M, N) tensor (possibly a row-strided view).
-    Launches on ``stream`` (default: torch's current stream) and returns
-    ``out`` without synchronising."""
+    ``bias`` is an optional contiguous (N,) tensor of the same dtype and
+    ``act`` one of "relu", "gelu_tanh", "none". ``out`` may be a preallocated
+    (M, N) tensor (possibly a row-strided view). Launches on ``stream``
+    (default: torch's current stream) and returns ``out`` without
+    synchronising."""
     import torch
     if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("a and b must both be float32 or both bfloat16")
@@ -181,11 +222,19 @@ def mmrelu(a, b, out=None, variant: int | None = None, stream=None):
         out = torch.empty((M, N), dtype=a.dtype, device=a.device)
     elif out.shape != (M, N) or out.dtype != a.dtype or out.device != a.device:
         raise ValueError("out has the wrong shape, dtype or device")
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(_ACTS)}")
+    if bias is not None and (bias.dtype != a.dtype or bias.device != a.device or bias.shape != (N,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous (N,) tensor of the inputs' dtype and device")
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    args = (a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, _ld(a), _ld(b), _ld(out), s.cuda_stream)
+    args = (a.data_ptr(), b.data_ptr(), bias.data_ptr() if bias is not None else 0, out.data_ptr(), M, N, K,
+            _ld(a), _ld(b), _ld(out), s.cuda_stream)
     if a.dtype == torch.float32:
-        rc = mmrelu_f32(*args) if variant is None else mmrelu_f32_variant(variant, *args)
+        rc = (mmrelu_fused_f32(_ACTS[act], *args) if variant is None
+              else mmrelu_fused_f32_variant(variant, _ACTS[act], *args))
     else:
-        rc = mmrelu_bf16(*args) if variant is None else mmrelu_bf16_variant(variant, *args)
+        rc = (mmrelu_fused_bf16(_ACTS[act], *args) if variant is None
+              else mmrelu_fused_bf16_variant(variant, _ACTS[act], *args))
     _check(rc, "mmrelu")
     return out

@@ -3,6 +3,8 @@
 // and the workgroup -> output-tile mapping.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <cstdint>
 
 namespace mmrelu {
@@ -92,6 +94,58 @@ __device__ inline __amdgpu_buffer_rsrc_t make_store_rsrc(void *base, int64_t byt
     const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(n), kBufferFormat);
 }
+// Fused epilogue, applied to each fp32 accumulator before the one store:
+// add the output column's bias (zero without a bias), then the activation.
+// Activation codes are those of mmrelu.h: 0 ReLU, 1 GeLU in its tanh form,
+// 2 none. GeLU's tanh form is 0.5 x (1 + tanh(u)), u = 0.79788456 (x +
+// 0.044715 x^3) ("Kernels, Triton, XLA", section "GeLU three ways: the case
+// for fusion"). Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), it is evaluated
+// as x / (1 + 2^(-2u log2 e)) with the hardware exp2 and reciprocal: no
+// branches, finite for every u (exp2 overflow gives -0 for very negative x,
+// underflow gives x), a few ulp from the exact value.
+__device__ inline float gelu_tanh(float x)
+{
+    const float u = 0.79788456f * (x + 0.044715f * x * x * x);
+    const float e = __builtin_amdgcn_exp2f(u * -2.88539008f);   // exp(-2u); 2.88539008 = 2 log2(e)
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+template <int ACT>
+__device__ inline float activate(float v)
+{
+    if constexpr (ACT == 0) return __builtin_fmaxf(v, 0.0f);
+    else if constexpr (ACT == 1) return gelu_tanh(v);
+    else return v;
+}
+// Runs f(std::integral_constant<int, act>) once: the caller's epilogue is
+// compiled once per activation, straight-line, and selected by one uniform
+// branch (a test per element would put hundreds of branches in the epilogue).
+template <typename F>
+__device__ inline void with_activation(int act, F &&f)
+{
+    if (act == 0) f(std::integral_constant<int, 0>{});
+    else if (act == 1) f(std::integral_constant<int, 1>{});
+    else f(std::integral_constant<int, 2>{});
+}
+// Resource over the bias elements of columns n0 .. N-1 (esize bytes each);
+// empty (every load reads 0) when there is no bias.
+__device__ inline __amdgpu_buffer_rsrc_t make_bias_rsrc(const void *bias, int n0, int N, int esize)
+{
+    const char *b = static_cast<const char *>(bias);
+    const int64_t bytes = b != nullptr ? static_cast<int64_t>(N - n0) * esize : 0;
+    return make_store_rsrc(const_cast<char *>(b != nullptr ? b + static_cast<int64_t>(n0) * esize : b), bytes);
+}
+// Bias of output column n0 + c (c relative to the tile) from a resource over
+// the columns n0 .. N-1 of the bias vector; columns past N read 0.
+__device__ inline float bias_f32(__amdgpu_buffer_rsrc_t r, int c)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<uint32_t>(c) * 4, 0, 0));
+}
+__device__ inline float bias_bf16(__amdgpu_buffer_rsrc_t r, int c)
+{
+    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<uint32_t>(c) * 2, 0, 0);
+    return __uint_as_float(h << 16);
+}
+
 __device__ inline void store_b128(__amdgpu_buffer_rsrc_t r, uint32_t voffset, u32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, voffset, 0, 0);

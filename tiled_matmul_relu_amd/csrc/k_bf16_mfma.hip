@@ -1,10 +1,11 @@
 // bf16 relu(A·B) on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16),
-// fp32 accumulation, ReLU on the fp32 sum, then one rounding to bf16 (nearest,
-// ties to even) in the store epilogue.
+// fp32 accumulation, the fused epilogue on the fp32 sum (optional per-column
+// bias, then ReLU by default, or GeLU's tanh form, or nothing), then one
+// rounding to bf16 (nearest, ties to even) in the store epilogue.
 //
 // The lecture's tiled recipe (one workgroup per output tile; K swept in slabs
-// staged in on-chip memory; fp32 accumulator; ReLU on the accumulator right
-// before the single, masked store), laid out for CDNA4:
+// staged in on-chip memory; fp32 accumulator; the activation on the
+// accumulator right before the single, masked store), laid out for CDNA4:
 //  * 256 x 256 output tile per workgroup of 4 wave64s (2 x 2); each wave owns
 //    a 128 x 128 sub-tile: 64 16x16 MFMA blocks, 256 fp32 accumulators per
 //    lane held in AGPRs (one wave per SIMD).
@@ -69,7 +70,8 @@ __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m)
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
+    const uint16_t *__restrict__ bias, int act)
 {
     using T = Bf16Tile<BM, BN, BK, STAGES, WAVES_M, WAVES_N>;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * T::kStage];
@@ -277,25 +279,44 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
         }
     }
 
-    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; ReLU
-    // on fp32, round to bf16, one 8-byte masked store.
+    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
+    // and activation on fp32, round to bf16, one 8-byte masked store. The
+    // bias values of the lane's columns are loaded once, up front, and only
+    // when there is a bias; stores go row block by row block, so the four
+    // column blocks of a row complete its lines back to back.
     const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0,
                                                       ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * 2);
+    float bj[T::NB][4];
+    if (bias != nullptr) {
+        const __amdgpu_buffer_rsrc_t rb = make_bias_rsrc(bias, n0, N, 2);
 #pragma unroll
-    for (int i = 0; i < T::MB; ++i) {
-        const int row = wm * T::WTM + i * 16 + t;
+        for (int j = 0; j < T::NB; ++j)
 #pragma unroll
-        for (int j = 0; j < T::NB; ++j) {
-            const int col = wn * T::WTN + j * 16 + 4 * g;
-            const f32x4 v = acc[i][j];
-            bf16x4 o;
+            for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rb, wn * T::WTN + j * 16 + 4 * g + r);
+    } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(__builtin_fmaxf(v[r], 0.0f));
-            const uint32_t off =
-                (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
-            store_b64(rc, off, __builtin_bit_cast(u32x2, o));
-        }
+        for (int j = 0; j < T::NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
     }
+    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+        for (int i = 0; i < T::MB; ++i) {
+            const int row = wm * T::WTM + i * 16 + t;
+#pragma unroll
+            for (int j = 0; j < T::NB; ++j) {
+                const int col = wn * T::WTN + j * 16 + 4 * g;
+                const f32x4 v = acc[i][j];
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[j][r]));
+                const uint32_t off =
+                    (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
+                store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+            }
+        }
+    });
 }
 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH, int GROUP_M>
@@ -305,7 +326,7 @@ hipError_t launch_bf16(const Problem &p, int64_t grid, hipStream_t stream)
     hipLaunchKernelGGL((mmrelu_bf16_mfma<BM, BN, BK, STAGES, WAVES_M, WAVES_N, PREFETCH>), dim3(static_cast<uint32_t>(grid)),
                        dim3(WAVES_M * WAVES_N * 64), 0, stream, static_cast<const uint16_t *>(p.A),
                        static_cast<const uint16_t *>(p.B), static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda,
-                       p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M);
+                       p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M, static_cast<const uint16_t *>(p.bias), p.act);
     return hipGetLastError();
 }
 

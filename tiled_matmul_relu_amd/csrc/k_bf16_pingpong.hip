@@ -9,8 +9,10 @@
 // The arithmetic is the lecture's tiled matmul with the fused activation
 // ("Kernels, Triton, XLA", section "Reductions and tiling", and the Chinese
 // notes' section 5.5): per output tile, K is swept in slabs staged in LDS,
-// fp32 accumulation (v_mfma_f32_16x16x32_bf16), ReLU on the accumulator, one
-// rounding to bf16 (nearest, ties to even), one masked store.
+// fp32 accumulation (v_mfma_f32_16x16x32_bf16), the fused epilogue on the
+// accumulator (optional per-column bias, then ReLU by default, or GeLU's
+// tanh form, or nothing), one rounding to bf16 (nearest, ties to even), one
+// masked store.
 //
 // Waves: wave w belongs to group w / 4; within a group, (wm, wn') =
 // ((w%4)/2, (w%4)%2) and the wave owns rows 128*wm .. +128 and columns
@@ -72,7 +74,8 @@ __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 
 template <int ORDER>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
-    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m)
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
+    const uint16_t *__restrict__ bias, int act)
 {
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsBytes / 2];
@@ -290,25 +293,44 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         }
     }
 
-    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; ReLU
-    // on fp32, round to bf16, one 8-byte masked store.
+    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
+    // and activation on fp32, round to bf16, one 8-byte masked store. The
+    // bias values of the lane's columns are loaded once, up front, and only
+    // when there is a bias; stores go row block by row block, so the four
+    // column blocks of a row complete its lines back to back.
     const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0,
                                                       ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * 2);
+    float bj[kNB][4];
+    if (bias != nullptr) {
+        const __amdgpu_buffer_rsrc_t rb = make_bias_rsrc(bias, n0, N, 2);
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) {
-        const int row = wm * 128 + i * 16 + t;
+        for (int j = 0; j < kNB; ++j)
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) {
-            const int col = wn * 64 + j * 16 + 4 * g;
-            const f32x4 v = acc[i][j];
-            bf16x4 o;
+            for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rb, wn * 64 + j * 16 + 4 * g + r);
+    } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(__builtin_fmaxf(v[r], 0.0f));
-            const uint32_t off =
-                (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
-            store_b64(rc, off, __builtin_bit_cast(u32x2, o));
-        }
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
     }
+    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            const int row = wm * 128 + i * 16 + t;
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) {
+                const int col = wn * 64 + j * 16 + 4 * g;
+                const f32x4 v = acc[i][j];
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[j][r]));
+                const uint32_t off =
+                    (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
+                store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+            }
+        }
+    });
 }
 
 template <int ORDER, int GROUP_M>
@@ -317,7 +339,8 @@ hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
     const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + kBN - 1) / kBN;
     hipLaunchKernelGGL((mmrelu_bf16_pingpong<ORDER>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
-                       static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M);
+                       static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M,
+                       static_cast<const uint16_t *>(p.bias), p.act);
     return hipGetLastError();
 }
 

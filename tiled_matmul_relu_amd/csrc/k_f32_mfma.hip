@@ -1,9 +1,11 @@
 // fp32 relu(A·B) on the gfx950 matrix cores (v_mfma_f32_16x16x4_f32): fp32
-// products accumulated in fp32 (no reduced-precision inputs).
+// products accumulated in fp32 (no reduced-precision inputs). The epilogue
+// adds the optional per-column bias and applies the activation (ReLU by
+// default, GeLU's tanh form, or none) before the one store.
 //
 // The lecture's tiled recipe (one workgroup per output tile; K swept in slabs
-// staged in on-chip memory; fp32 accumulator; ReLU on the accumulator right
-// before the single, masked store), laid out for CDNA4:
+// staged in on-chip memory; fp32 accumulator; the activation on the
+// accumulator right before the single, masked store), laid out for CDNA4:
 //  * A BM x BN tile per workgroup of WAVES_M x WAVES_N wave64s; each wave owns
 //    a (BM/WAVES_M) x (BN/WAVES_N) sub-tile held in MFMA accumulators.
 //  * K slabs are copied global -> LDS by the buffer unit directly (no VGPR
@@ -64,7 +66,8 @@ __device__ inline int swz_b(int k) { return ((k >> 2) & 3) << 2; }
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool ALIGNED>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 2) void mmrelu_f32_mfma(
     const float *__restrict__ A, const float *__restrict__ B, float *__restrict__ C,
-    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m)
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
+    const float *__restrict__ bias, int act)
 {
     using T = F32Tile<BM, BN, BK, WAVES_M, WAVES_N, ALIGNED>;
     __shared__ __attribute__((aligned(1024))) float lds[2 * T::kStage];
@@ -204,34 +207,50 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 2) void mmrelu_f32_mfma(
         __syncthreads();
     }
 
-    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; ReLU
-    // on the fp32 accumulators, one masked store.
+    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
+    // and activation on the fp32 accumulators, one masked store.
     const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0,
                                                       ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * 4);
+    float bj[T::NB][4];   // the bias of the lane's columns, loaded once, only when there is one
+    if (bias != nullptr) {
+        const __amdgpu_buffer_rsrc_t rb = make_bias_rsrc(bias, n0, N, 4);
 #pragma unroll
-    for (int i = 0; i < T::MB; ++i) {
-        const int row = wm * T::WTM + i * 16 + t;
-        const bool row_ok = m0 + row < M;
+        for (int j = 0; j < T::NB; ++j)
 #pragma unroll
-        for (int j = 0; j < T::NB; ++j) {
-            const int col = wn * T::WTN + j * 16 + 4 * g;
-            f32x4 v = acc[i][j];
+            for (int r = 0; r < 4; ++r) bj[j][r] = bias_f32(rb, wn * T::WTN + j * 16 + 4 * g + r);
+    } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaxf(v[r], 0.0f);
-            if (ALIGNED) {
-                const uint32_t off =
-                    (row_ok && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 4) : kOutOfRange;
-                store_b128(rc, off, __builtin_bit_cast(u32x4, v));
-            } else {
+        for (int j = 0; j < T::NB; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
+    }
+    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+        for (int i = 0; i < T::MB; ++i) {
+            const int row = wm * T::WTM + i * 16 + t;
+            const bool row_ok = m0 + row < M;
+#pragma unroll
+            for (int j = 0; j < T::NB; ++j) {
+                const int col = wn * T::WTN + j * 16 + 4 * g;
+                f32x4 v = acc[i][j];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(v[r] + bj[j][r]);
+                if (ALIGNED) {
                     const uint32_t off =
-                        (row_ok && n0 + col + r < N) ? static_cast<uint32_t>((row * ldc + col + r) * 4) : kOutOfRange;
-                    store_b32(rc, off, __float_as_uint(v[r]));
+                        (row_ok && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 4) : kOutOfRange;
+                    store_b128(rc, off, __builtin_bit_cast(u32x4, v));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t off =
+                            (row_ok && n0 + col + r < N) ? static_cast<uint32_t>((row * ldc + col + r) * 4) : kOutOfRange;
+                        store_b32(rc, off, __float_as_uint(v[r]));
+                    }
                 }
             }
         }
-    }
+    });
 }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool ALIGNED, int GROUP_M>
@@ -241,7 +260,7 @@ hipError_t launch_f32(const Problem &p, int64_t grid, hipStream_t stream)
     hipLaunchKernelGGL((mmrelu_f32_mfma<BM, BN, BK, WAVES_M, WAVES_N, ALIGNED>), dim3(static_cast<uint32_t>(grid)),
                        dim3(WAVES_M * WAVES_N * 64), 0, stream, static_cast<const float *>(p.A),
                        static_cast<const float *>(p.B), static_cast<float *>(p.C), p.M, p.N, p.K, p.lda, p.ldb,
-                       p.ldc, tiles_m, tiles_n, GROUP_M);
+                       p.ldc, tiles_m, tiles_n, GROUP_M, static_cast<const float *>(p.bias), p.act);
     return hipGetLastError();
 }
 

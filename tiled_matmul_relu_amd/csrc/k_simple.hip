@@ -5,8 +5,11 @@
 // dimension the interface allows and serves as the reference layout for the
 // matrix-core kernels. Edge tiles: loads outside M, N or K read 0 (the masked
 // loads with other=0 of the lecture's listing), stores outside M x N are
-// skipped, so C outside the window is never written.
+// skipped, so C outside the window is never written. The epilogue adds the
+// optional per-column bias to the fp32 accumulator and applies the
+// activation (ReLU, GeLU's tanh form or none) before the store.
 #include "kernels.hpp"
+#include "device_common.hpp"
 #include "../../include/mmrelu.h"
 
 namespace mmrelu {
@@ -30,7 +33,7 @@ template <> __device__ inline uint16_t from_f32<uint16_t>(float v) {
 template <typename T>
 __global__ __launch_bounds__(THREADS) void mmrelu_simple_64x64x16(
     const T *__restrict__ A, const T *__restrict__ B, T *__restrict__ C,
-    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_n)
+    int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_n, const T *__restrict__ bias, int act)
 {
     __shared__ float As[BK][BM + 4];   // A slab stored k-major: As[k][m]
     __shared__ float Bs[BK][BN + 4];   // B slab as in memory:   Bs[k][n]
@@ -73,16 +76,25 @@ __global__ __launch_bounds__(THREADS) void mmrelu_simple_64x64x16(
         }
         __syncthreads();
     }
+    float bj[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + ty * 4 + i;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + tx * 4 + j;
-            if (n < N) C[m * ldc + n] = from_f32<T>(fmaxf(acc[i][j], 0.0f));
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + tx * 4 + j;
+        bj[j] = (bias != nullptr && n < N) ? to_f32(bias[n]) : 0.0f;
     }
+    with_activation(act, [&](auto act_c) {
+        constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + ty * 4 + i;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t n = n0 + tx * 4 + j;
+                if (n < N) C[m * ldc + n] = from_f32<T>(activate<ACT>(acc[i][j] + bj[j]));
+            }
+        }
+    });
 }
 
 template <typename T>
@@ -91,7 +103,7 @@ hipError_t launch_simple(const Problem &p, int64_t grid, hipStream_t stream)
     const int tiles_n = (p.N + BN - 1) / BN;
     hipLaunchKernelGGL(mmrelu_simple_64x64x16<T>, dim3(static_cast<uint32_t>(grid)), dim3(THREADS), 0, stream,
                        static_cast<const T *>(p.A), static_cast<const T *>(p.B), static_cast<T *>(p.C),
-                       p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_n);
+                       p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_n, static_cast<const T *>(p.bias), p.act);
     return hipGetLastError();
 }
 

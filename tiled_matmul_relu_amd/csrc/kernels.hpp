@@ -13,6 +13,8 @@ struct Problem {
     void *C;
     int32_t M, N, K;
     int64_t lda, ldb, ldc;
+    const void *bias;   // N elements of the input dtype, or null
+    int32_t act;        // activation code of mmrelu.h (0 ReLU, 1 GeLU tanh, 2 none)
 };
 
 // Launches one variant over `grid` workgroups on `stream`; returns the launch

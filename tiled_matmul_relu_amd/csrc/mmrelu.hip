@@ -153,14 +153,16 @@ int fill_plan(const Variant *v, int32_t index, int64_t M, int64_t N, int32_t cus
     return MMRELU_OK;
 }
 
-int run(int dtype, int32_t variant, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
-        int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+int run(int dtype, int32_t variant, int act, const void *A, const void *B, const void *bias, void *C, int64_t M,
+        int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
 {
     const size_t esize = dtype == MMRELU_DTYPE_F32 ? 4 : 2;
+    if (act != MMRELU_ACT_RELU && act != MMRELU_ACT_GELU_TANH && act != MMRELU_ACT_NONE) return MMRELU_ERR_INVALID_VALUE;
     int rc = check_shape(M, N, K, lda, ldb, ldc);
     if (rc != MMRELU_OK) return rc;
     rc = check_pointers(A, B, C, M, N, K, esize);
     if (rc != MMRELU_OK) return rc;
+    if (bias != nullptr && reinterpret_cast<uintptr_t>(bias) % esize != 0) return MMRELU_ERR_MISALIGNED;
     if (variant < 0) variant = choose_variant(dtype, M, N, K, lda, ldb, ldc, A, B, C, device_cus());
     const Variant *v = variant_at(dtype, variant);
     if (v == nullptr) return MMRELU_ERR_INVALID_VALUE;
@@ -169,7 +171,8 @@ int run(int dtype, int32_t variant, const void *A, const void *B, void *C, int64
     mmrelu_plan_t plan;
     rc = fill_plan(v, variant, M, N, kDefaultCus, &plan);
     if (rc != MMRELU_OK) return rc;
-    Problem p{A, B, C, static_cast<int32_t>(M), static_cast<int32_t>(N), static_cast<int32_t>(K), lda, ldb, ldc};
+    Problem p{A, B, C, static_cast<int32_t>(M), static_cast<int32_t>(N), static_cast<int32_t>(K), lda, ldb, ldc,
+              bias, act};
     hipError_t e = v->launch(p, plan.grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MMRELU_OK : MMRELU_ERR_LAUNCH;
 }
@@ -184,34 +187,61 @@ extern "C" {
 int mmrelu_f32(const float *A, const float *B, float *C, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int64_t ldc, void *stream)
 {
-    return run(MMRELU_DTYPE_F32, -1, A, B, C, M, N, K, lda, ldb, ldc, stream);
+    return run(MMRELU_DTYPE_F32, -1, MMRELU_ACT_RELU, A, B, nullptr, C, M, N, K, lda, ldb, ldc, stream);
 }
 
 int mmrelu_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, void *stream)
 {
-    return run(MMRELU_DTYPE_BF16, -1, A, B, C, M, N, K, lda, ldb, ldc, stream);
+    return run(MMRELU_DTYPE_BF16, -1, MMRELU_ACT_RELU, A, B, nullptr, C, M, N, K, lda, ldb, ldc, stream);
 }
 
 int mmrelu_f32_variant(int32_t variant, const float *A, const float *B, float *C, int64_t M, int64_t N,
                        int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
 {
     if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
-    return run(MMRELU_DTYPE_F32, variant, A, B, C, M, N, K, lda, ldb, ldc, stream);
+    return run(MMRELU_DTYPE_F32, variant, MMRELU_ACT_RELU, A, B, nullptr, C, M, N, K, lda, ldb, ldc, stream);
 }
 
 int mmrelu_bf16_variant(int32_t variant, const uint16_t *A, const uint16_t *B, uint16_t *C, int64_t M,
                         int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
 {
     if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
-    return run(MMRELU_DTYPE_BF16, variant, A, B, C, M, N, K, lda, ldb, ldc, stream);
+    return run(MMRELU_DTYPE_BF16, variant, MMRELU_ACT_RELU, A, B, nullptr, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_fused_f32(int act, const float *A, const float *B, const float *bias, float *C, int64_t M, int64_t N,
+                     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    return run(MMRELU_DTYPE_F32, -1, act, A, B, bias, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, uint16_t *C, int64_t M,
+                      int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    return run(MMRELU_DTYPE_BF16, -1, act, A, B, bias, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_fused_f32_variant(int32_t variant, int act, const float *A, const float *B, const float *bias, float *C,
+                             int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return run(MMRELU_DTYPE_F32, variant, act, A, B, bias, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_fused_bf16_variant(int32_t variant, int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                              uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                              void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return run(MMRELU_DTYPE_BF16, variant, act, A, B, bias, C, M, N, K, lda, ldb, ldc, stream);
 }
 
 const char *mmrelu_status_string(int status)
 {
     switch (status) {
     case MMRELU_OK: return "ok";
-    case MMRELU_ERR_INVALID_VALUE: return "invalid value (size, leading dimension or variant)";
+    case MMRELU_ERR_INVALID_VALUE: return "invalid value (size, leading dimension, variant or activation)";
     case MMRELU_ERR_NULL_POINTER: return "null pointer";
     case MMRELU_ERR_MISALIGNED: return "pointer not aligned to its element size";
     case MMRELU_ERR_LAUNCH: return "kernel launch failed";
