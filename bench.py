@@ -239,6 +239,10 @@ def main():
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: per-call statistics (mean, median, P95, algorithmic GB/s, "
                          "grid and wave quantization) of all five workloads, one JSON line each")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: square sizes 256..8192 and skinny shapes (M or N of "
+                         "1..64, the others 8192) in both dtypes, per-call statistics with the bounding roofline "
+                         "(MFMA or HBM) and the fraction of it reached, one JSON line each")
     ap.add_argument("--act", choices=["relu", "gelu_tanh", "none"], default="relu",
                     help="with --all-configs: the fused epilogue's activation")
     ap.add_argument("--bias", action="store_true", help="with --all-configs: add a per-column bias")
@@ -256,6 +260,30 @@ def main():
         for ident, cfg in sorted(datagen.CONFIGS.items()):
             print(json.dumps({"config": ident, **per_call_stats(cfg, args.steps, args.warmup, torch, mm, datagen,
                                                                 act=args.act, bias=args.bias)}), flush=True)
+        return
+
+    if args.sweep:
+        import torch
+        import datagen
+        import tiled_matmul_relu_amd as mm
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        mm.load_library()
+        for dtype in ("f32", "bf16"):
+            shapes = [(n, n, n) for n in (256, 512, 1024, 2048, 4096, 8192)]
+            shapes += [(m, 8192, 8192) for m in (1, 8, 16, 32, 64)] + [(8192, n, 8192) for n in (1, 16, 64)]
+            for (M, N, K) in shapes:
+                cfg = datagen.Config(0, f"{dtype}_{M}x{N}x{K}", dtype, M, N, K, K, N, N, "normal_over_sqrtk")
+                steps = 40 if cfg.flops > 2e11 else 100
+                r = per_call_stats(cfg, steps, 20, torch, mm, datagen)
+                peak = PEAK_TFLOPS[dtype]
+                t_mfma = cfg.flops / (peak * 1e12) * 1e3
+                t_hbm = cfg.elem_bytes * (M * K + K * N + M * N) / (HBM_PEAK_GBS * 1e9) * 1e3
+                r["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+                r["roofline_frac"] = round(max(t_mfma, t_hbm) / r["median_ms"], 4)
+                r["pct_of_hbm_peak"] = round(100 * r["alg_gbs_median"] / HBM_PEAK_GBS, 2)
+                print(json.dumps(r), flush=True)
         return
 
     if args.record_traffic:
