@@ -126,8 +126,11 @@ typedef struct {
 /* Fill *out for a call of this dtype and shape. cus = 0 uses the current
  * device's compute-unit count when a device is present, else 256. Returns a
  * status as above (arguments are validated the same way, pointers aside).
- * The choice: among the dtype's matrix-core kernels at a large and a small
- * tile that accept the layout, the one with the least estimated time on the
+ * The choice: for M <= 64 with an aligned layout, the skinny kernel of the
+ * smallest row count that covers M (16, 32 or 64 rows; it splits K over the
+ * eight waves of a workgroup so a 32-column strip of B streams from memory
+ * once). Otherwise, among the dtype's matrix-core kernels at a large and a
+ * small tile that accept the layout, the one with the least estimated time on the
  * busiest compute unit, ceil(tiles / cus) tiles times the tile's outputs
  * times the kernel's measured relative cost per output; layouts no
  * matrix-core kernel accepts use the plain tiled kernel (variant 0). The
@@ -148,7 +151,9 @@ int mmrelu_plan_variant(int dtype, int32_t variant, int64_t M, int64_t N, int64_
 int mmrelu_wave_quantization(int64_t blocks, int64_t slots, int64_t *waves, int64_t *idle_last);
 
 /* As mmrelu_f32 / mmrelu_bf16 but with an explicit kernel variant instead of
- * the planner's choice (for tests and tuning). Same checks and semantics. */
+ * the planner's choice (for tests and tuning). Same checks and semantics; a
+ * skinny variant given more rows than it covers returns
+ * MMRELU_ERR_INVALID_VALUE. */
 int mmrelu_f32_variant(int32_t variant, const float *A, const float *B, float *C,
                        int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc, void *stream);

@@ -95,6 +95,17 @@ def test_fused_entry_points_validate(dtype):
     assert fused(E.ACT_GELU_TANH, A, B, 0, C, 4, 0, 4, 4, 4, 4) == E.MMRELU_OK
 
 
+def test_planner_picks_skinny_kernels_for_few_rows():
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        for M, rows in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
+            p = mm.mmrelu_plan(dt, M, 8192, 8192, 8192, 8192, 8192, cus=256)
+            assert "skinny" in p["name"] and p["block_m"] == rows and p["grid"] == 8192 // 32, (M, p["name"])
+        assert "skinny" not in mm.mmrelu_plan(dt, 65, 8192, 8192, 8192, 8192, 8192, cus=256)["name"]
+        # an odd leading dimension needs a kernel that accepts any layout
+        p = mm.mmrelu_plan(dt, 16, 8191, 8192, 8192, 8191, 8191, cus=256)
+        assert "skinny" not in p["name"]
+
+
 def test_variant_entry_points_validate():
     assert mm.mmrelu_f32_variant(-1, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
     assert mm.mmrelu_f32_variant(99, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
@@ -106,6 +117,12 @@ def test_variant_entry_points_validate():
     assert needs_align
     for v in needs_align:
         assert mm.mmrelu_f32_variant(v, A, B, C, 5, 5, 5, 5, 5, 5) == mm.MMRELU_ERR_INVALID_VALUE
+    # a skinny variant covers at most block_m rows (checked before any launch)
+    for v in range(nv):
+        p = mm.mmrelu_plan_variant(0, v, 8, 8, 8, 8, 8, 8)
+        if "skinny" in p["name"]:
+            m = p["block_m"] + 1
+            assert mm.mmrelu_f32_variant(v, A, B, C, m, 8, 8, 8, 8, 8) == mm.MMRELU_ERR_INVALID_VALUE
 
 
 def test_wave_quantization_matches_lecture_arithmetic():

@@ -90,8 +90,11 @@ def variants(dtype):
     return list(range(mm.mmrelu_num_variants(dtype)))
 
 
-def accepts(dtype, v, N, K, lda, ldb, ldc):
-    name = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)["name"]
+def accepts(dtype, v, N, K, lda, ldb, ldc, M=1):
+    plan = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)
+    name = plan["name"]
+    if "skinny" in name and M > plan["block_m"]:
+        return False                      # covers at most block_m rows
     if "simple" in name or "unaligned" in name:
         return True
     q = 4 if dtype == mm.DTYPE_F32 else 8
@@ -112,8 +115,8 @@ BF16_SHAPES = [
 @pytest.mark.parametrize("variant", variants(mm.DTYPE_F32))
 def test_f32_variants_small(variant, shape):
     M, N, K = shape
-    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N):
-        pytest.skip("variant needs 16-byte rows")
+    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N, M=M):
+        pytest.skip("variant needs 16-byte rows, or covers fewer rows")
     a = datagen.normal_f32(10 + M, M, K, 1 / math.sqrt(K))
     b = datagen.normal_f32(20 + N, K, N, 1 / math.sqrt(K))
     c, _ = run(a, b, M, N, K, K, N, variant=variant)
@@ -124,8 +127,8 @@ def test_f32_variants_small(variant, shape):
 @pytest.mark.parametrize("variant", variants(mm.DTYPE_BF16))
 def test_bf16_variants_small(variant, shape):
     M, N, K = shape
-    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N):
-        pytest.skip("variant needs 16-byte rows")
+    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N, M=M):
+        pytest.skip("variant needs 16-byte rows, or covers fewer rows")
     a = datagen.f32_to_bf16_bits(datagen.normal_f32(30 + M, M, K, 1 / math.sqrt(K)))
     b = datagen.f32_to_bf16_bits(datagen.normal_f32(40 + N, K, N, 1 / math.sqrt(K)))
     c, _ = run(a, b, M, N, K, K, N, variant=variant)
@@ -135,8 +138,8 @@ def test_bf16_variants_small(variant, shape):
 @pytest.mark.parametrize("variant", variants(mm.DTYPE_F32))
 def test_f32_exact_integers_bit_exact(variant):
     M, N, K = 200, 132, 300
-    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N):
-        pytest.skip("variant needs 16-byte rows")
+    if not accepts(mm.DTYPE_F32, variant, N, K, K, N, N, M=M):
+        pytest.skip("variant needs 16-byte rows, or covers fewer rows")
     a = datagen.small_int_f32(51, M, K)
     b = datagen.small_int_f32(52, K, N)
     c, _ = run(a, b, M, N, K, K, N, variant=variant)
@@ -149,8 +152,8 @@ def test_bf16_exact_integers_round_to_nearest_even(variant):
     rounded to bf16 (nearest, ties to even) bit for bit: pins the epilogue
     rounding mode."""
     M, N, K = 136, 264, 520
-    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N):
-        pytest.skip("variant needs 16-byte rows")
+    if not accepts(mm.DTYPE_BF16, variant, N, K, K, N, N, M=M):
+        pytest.skip("variant needs 16-byte rows, or covers fewer rows")
     a = datagen.f32_to_bf16_bits(datagen.small_int_f32(61, M, K))
     b = datagen.f32_to_bf16_bits(datagen.small_int_f32(62, K, N))
     r = oracle.mmrelu(a, b)
@@ -174,7 +177,8 @@ def test_guard_band_and_padded_leading_dimensions(dtype):
         a, b, dt = a32, b32, mm.DTYPE_F32
     r = oracle.mmrelu(a, b, M=M, N=N, K=K, lda=lda, ldb=ldb)
     for v in variants(dt):
-        assert accepts(dt, v, N, K, lda, ldb, ldc)
+        if not accepts(dt, v, N, K, lda, ldb, ldc, M=M):
+            continue                      # a skinny kernel: covers fewer rows
         c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, variant=v, guard=3)
         if dtype == "bf16":
             check_bf16(c, r)
@@ -205,7 +209,7 @@ def test_zero_inputs_give_zero_outputs(dtype):
     a = np.zeros((M, K), np.float32 if dtype == "f32" else np.uint16)
     b = np.zeros((K, N), a.dtype)
     for v in variants(kind):
-        if not accepts(kind, v, N, K, K, N, N):
+        if not accepts(kind, v, N, K, K, N, N, M=M):
             continue
         c, _ = run(a, b, M, N, K, K, N, variant=v)
         vals = c if dtype == "f32" else datagen.bf16_bits_to_f32(c)
