@@ -106,6 +106,32 @@ def test_planner_picks_skinny_kernels_for_few_rows():
         assert "skinny" not in p["name"]
 
 
+def test_planner_picks_skinny_kernels_for_few_columns():
+    q = {mm.DTYPE_F32: 4, mm.DTYPE_BF16: 8}
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        for N, cols in ((q[dt], 16), (16, 16), (24, 32), (32, 32), (40, 64), (64, 64)):
+            p = mm.mmrelu_plan(dt, 8192, N, 8192, 8192, N, N, cus=256)
+            assert "skinny" in p["name"] and p["block_n"] == cols and p["block_m"] == 32, (N, p["name"])
+            assert p["grid"] == 8192 // 32
+        assert "skinny" not in mm.mmrelu_plan(dt, 8192, 72, 8192, 8192, 72, 72, cus=256)["name"]
+        # both small: the smaller dimension decides
+        assert mm.mmrelu_plan(dt, 16, 64, 8192, 8192, 64, 64, cus=256)["block_m"] == 16
+        p = mm.mmrelu_plan(dt, 64, 16, 8192, 8192, 16, 16, cus=256)
+        assert (p["block_m"], p["block_n"]) == (32, 16)
+
+
+def test_skinny_variants_tile_any_shape():
+    """A skinny variant covers a shape of any size with a grid of its tiles."""
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        for v in range(mm.mmrelu_num_variants(dt)):
+            p = mm.mmrelu_plan_variant(dt, v, 1000, 264, 512, 512, 264, 264, cus=256)
+            if "skinny" not in p["name"]:
+                continue
+            tm = (1000 + p["block_m"] - 1) // p["block_m"]
+            tn = (264 + p["block_n"] - 1) // p["block_n"]
+            assert (p["tiles_m"], p["tiles_n"], p["grid"]) == (tm, tn, tm * tn), p["name"]
+
+
 def test_variant_entry_points_validate():
     assert mm.mmrelu_f32_variant(-1, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
     assert mm.mmrelu_f32_variant(99, A, B, C, 4, 4, 4, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
@@ -117,12 +143,6 @@ def test_variant_entry_points_validate():
     assert needs_align
     for v in needs_align:
         assert mm.mmrelu_f32_variant(v, A, B, C, 5, 5, 5, 5, 5, 5) == mm.MMRELU_ERR_INVALID_VALUE
-    # a skinny variant covers at most block_m rows (checked before any launch)
-    for v in range(nv):
-        p = mm.mmrelu_plan_variant(0, v, 8, 8, 8, 8, 8, 8)
-        if "skinny" in p["name"]:
-            m = p["block_m"] + 1
-            assert mm.mmrelu_f32_variant(v, A, B, C, m, 8, 8, 8, 8, 8) == mm.MMRELU_ERR_INVALID_VALUE
 
 
 def test_wave_quantization_matches_lecture_arithmetic():

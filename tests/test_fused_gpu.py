@@ -89,8 +89,6 @@ def variants(dtype):
 def accepts(dtype, v, N, K, lda, ldb, ldc, M=1):
     plan = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)
     name = plan["name"]
-    if "skinny" in name and M > plan["block_m"]:
-        return False                      # covers at most block_m rows
     if "simple" in name or "unaligned" in name:
         return True
     q = 4 if dtype == mm.DTYPE_F32 else 8

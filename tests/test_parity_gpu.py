@@ -93,8 +93,6 @@ def variants(dtype):
 def accepts(dtype, v, N, K, lda, ldb, ldc, M=1):
     plan = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)
     name = plan["name"]
-    if "skinny" in name and M > plan["block_m"]:
-        return False                      # covers at most block_m rows
     if "simple" in name or "unaligned" in name:
         return True
     q = 4 if dtype == mm.DTYPE_F32 else 8
@@ -178,7 +176,7 @@ def test_guard_band_and_padded_leading_dimensions(dtype):
     r = oracle.mmrelu(a, b, M=M, N=N, K=K, lda=lda, ldb=ldb)
     for v in variants(dt):
         if not accepts(dt, v, N, K, lda, ldb, ldc, M=M):
-            continue                      # a skinny kernel: covers fewer rows
+            continue
         c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, variant=v, guard=3)
         if dtype == "bf16":
             check_bf16(c, r)

@@ -1,11 +1,13 @@
-"""Parity of the skinny-M kernels (M <= 64) with the fp64 oracle (needs the
-GPU; every call goes through the C-ABI).
+"""Parity of the skinny kernels (few rows: M <= 64, or few columns: N <= 64)
+with the fp64 oracle (needs the GPU; every call goes through the C-ABI).
 
 The skinny kernels split K over eight waves per workgroup and sum the eight
 partial tiles at the end, so their summation order differs from the
 large-tile kernels'; the tolerances are the same: fp32 max |C - R| <=
 1e-4 * sqrt(K), bf16 relative Frobenius <= 1e-2 with the elementwise bound
-2^-8 |R| + 1e-6, and exact results on small-integer inputs.
+2^-8 |R| + 1e-6, and exact results on small-integer inputs. Every skinny
+variant tiles any shape, so each is also run on shapes many tiles wide and
+tall.
 """
 import math
 
@@ -19,7 +21,7 @@ import tiled_matmul_relu_amd as mm
 
 pytestmark = pytest.mark.gpu
 
-SKINNY = {"f32": [5, 6, 7], "bf16": [5, 6, 7]}        # covering up to 16, 32, 64 rows
+SKINNY = [5, 6, 7, 8, 9, 10]  # tiles 16x32, 32x32, 64x32 (few rows), 32x16, 32x32, 32x64 (few columns)
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:
@@ -81,22 +83,54 @@ MS = [1, 3, 16, 17, 32, 33, 64]
 NK = [(32, 8), (264, 72), (1000, 1032), (520, 4096)]
 
 
+def run_all_skinny(dtype, a, b, M, N, K, r):
+    for v in SKINNY:
+        print(f"{dtype} {M}x{N}x{K} variant={v}", flush=True)
+        check(run(a, b, M, N, K, K, N, variant=v)[0], r, K, dtype)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", MS)
-def test_skinny_shapes_every_variant(dtype, M):
+def test_skinny_rows_every_variant(dtype, M):
     kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
     for si, (N, K) in enumerate(NK):
         a, b = inputs(dtype, M, N, K, 900 + 10 * M + si)
         r = oracle.mmrelu(a, b)
         plan = mm.mmrelu_plan(kind, M, N, K, K, N, N)
-        assert "skinny" in plan["name"] and plan["block_m"] >= M, plan["name"]
-        print(f"{dtype} M={M} N={N} K={K} planner", flush=True)
+        assert "skinny" in plan["name"], plan["name"]
+        print(f"{dtype} M={M} N={N} K={K} planner {plan['name']}", flush=True)
         check(run(a, b, M, N, K, K, N)[0], r, K, dtype)
-        for v in SKINNY[dtype]:
-            if M > mm.mmrelu_plan_variant(kind, v, 8, 8, 8, 8, 8, 8)["block_m"]:
-                continue
-            print(f"{dtype} M={M} N={N} K={K} variant={v}", flush=True)
-            check(run(a, b, M, N, K, K, N, variant=v)[0], r, K, dtype)
+        run_all_skinny(dtype, a, b, M, N, K, r)
+
+
+NS = {"f32": [4, 12, 16, 24, 32, 40, 64], "bf16": [8, 16, 24, 32, 40, 64]}
+MK = [(40, 8), (264, 72), (1000, 1032), (72, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ni", range(7))
+def test_skinny_columns_every_variant(dtype, ni):
+    if ni >= len(NS[dtype]):
+        pytest.skip("fewer column counts for this dtype")
+    N = NS[dtype][ni]
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    for si, (M, K) in enumerate(MK):
+        a, b = inputs(dtype, M, N, K, 1900 + 10 * N + si)
+        r = oracle.mmrelu(a, b)
+        plan = mm.mmrelu_plan(kind, M, N, K, K, N, N)
+        assert "skinny" in plan["name"], plan["name"]
+        print(f"{dtype} M={M} N={N} K={K} planner {plan['name']}", flush=True)
+        check(run(a, b, M, N, K, K, N)[0], r, K, dtype)
+        run_all_skinny(dtype, a, b, M, N, K, r)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_skinny_variants_tile_large_shapes(dtype):
+    """Every skinny variant on shapes many tiles tall and wide, with ragged
+    edges in both directions."""
+    for si, (M, N, K) in enumerate([(300, 200, 264), (129, 520, 1032)]):
+        a, b = inputs(dtype, M, N, K, 961 + si)
+        run_all_skinny(dtype, a, b, M, N, K, oracle.mmrelu(a, b))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -115,26 +149,31 @@ def test_skinny_exact_integers(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_skinny_guard_band_padded(dtype):
+@pytest.mark.parametrize("M,N", [(40, 264), (264, 40)], ids=["rows", "columns"])
+def test_skinny_guard_band_padded(dtype, M, N):
     """Padded lda/ldb/ldc (NaN padding in A and B must never be read) and rows
     around C: nothing outside the window is written."""
-    M, N, K = 40, 264, 136
+    K = 136
     lda, ldb, ldc = K + 8, N + 16, N + 24
     a32 = datagen.pad_rows(datagen.normal_f32(931, M, K, 1 / math.sqrt(K)), lda, fill=np.nan)
     b32 = datagen.pad_rows(datagen.normal_f32(932, K, N, 1 / math.sqrt(K)), ldb, fill=np.nan)
     a, b = (a32, b32) if dtype == "f32" else (datagen.f32_to_bf16_bits(a32), datagen.f32_to_bf16_bits(b32))
     r = oracle.mmrelu(a, b, M=M, N=N, K=K, lda=lda, ldb=ldb)
-    c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, guard=3)
-    check(c, r, K, dtype)
-    wf = whole.astype(np.float32) if dtype == "f32" else datagen.bf16_bits_to_f32(whole)
-    outside = np.ones(wf.shape, bool)
-    outside[3:3 + M, :N] = False
-    assert np.all(np.isnan(wf[outside]))
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    assert "skinny" in mm.mmrelu_plan(kind, M, N, K, lda, ldb, ldc)["name"]
+    for v in [None] + SKINNY:
+        c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, variant=v, guard=3)
+        check(c, r, K, dtype)
+        wf = whole.astype(np.float32) if dtype == "f32" else datagen.bf16_bits_to_f32(whole)
+        outside = np.ones(wf.shape, bool)
+        outside[3:3 + M, :N] = False
+        assert np.all(np.isnan(wf[outside])), f"variant {v} wrote outside the window"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_skinny_fused_epilogue(dtype):
-    M, N, K = 24, 520, 264
+@pytest.mark.parametrize("M,N", [(24, 520), (520, 24)], ids=["rows", "columns"])
+def test_skinny_fused_epilogue(dtype, M, N):
+    K = 264
     a, b = inputs(dtype, M, N, K, 941)
     bias = datagen.normal_f32(943, 1, N, 0.5).ravel()
     if dtype == "bf16":
@@ -150,22 +189,13 @@ def test_skinny_fused_epilogue(dtype):
             assert np.all(np.abs(cf - r) <= 2.0 ** -8 * np.abs(r) + 4e-6)
 
 
-def test_variant_rejects_more_rows_than_it_covers():
-    a = torch.zeros(65, 64, device="cuda")
-    b = torch.zeros(64, 64, device="cuda")
-    c = torch.zeros(65, 64, device="cuda")
-    s = torch.cuda.current_stream().cuda_stream
-    rc = mm.mmrelu_f32_variant(7, a.data_ptr(), b.data_ptr(), c.data_ptr(), 65, 64, 64, 64, 64, 64, s)
-    assert rc == mm.MMRELU_ERR_INVALID_VALUE
-    rc = mm.mmrelu_f32_variant(7, a.data_ptr(), b.data_ptr(), c.data_ptr(), 64, 64, 64, 64, 64, 64, s)
-    assert rc == mm.MMRELU_OK
-    torch.cuda.synchronize()
-
-
-@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 16, 8192, 8192), ("f32", 64, 4096, 4096)])
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 16, 8192, 8192), ("f32", 64, 4096, 4096),
+                                         ("bf16", 8192, 16, 8192), ("f32", 4096, 64, 4096)])
 def test_skinny_full_size(dtype, M, N, K):
     """Full compare at the sweep's skinny sizes (the oracle runs ~1e9 MACs)."""
     print(f"skinny full size {dtype} {M}x{N}x{K}", flush=True)
     a, b = inputs(dtype, M, N, K, 951)
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    assert "skinny" in mm.mmrelu_plan(kind, M, N, K, K, N, N)["name"]
     c, _ = run(a, b, M, N, K, K, N)
     check(c, oracle.mmrelu(a, b), K, dtype)

@@ -1,31 +1,41 @@
-// relu(A·B) (and the fused epilogues) for skinny M (M <= 64), where the work
-// is bound by reading B from HBM once, not by the matrix cores: a 64 x 8192 x
-// 8192 bf16 product is 8.6 GFLOP (3.4 us of MFMA at peak) but 128 MB of B
-// (16.8 us at 8 TB/s).
+// relu(A·B) (and the fused epilogues) for skinny products, where the work is
+// bound by reading the large operand from HBM once, not by the matrix cores:
+//  * skinny M (M <= 64): a 64 x 8192 x 8192 bf16 product is 8.6 GFLOP (3.4 us
+//    of MFMA at peak) but 128 MB of B (16.8 us at 8 TB/s);
+//  * skinny N (N <= 64): the mirror image, 128 MB of A for an 8192 x 64 C.
 //
 // The arithmetic is the same tiled product with the activation fused into
 // the one store ("Kernels, Triton, XLA", section "Reductions and tiling"); the
 // tile is shaped for a memory-bound product:
-//  * One workgroup per 32-column strip of B and C (N = 8192 gives 256
-//    workgroups, one per CU), covering all M <= 16 * MB rows. Every workgroup
-//    reads all of A, which is small and stays in L2.
+//  * One workgroup per (16 MB) x (16 NB) tile of C: MB = 1, 2, 4 row blocks
+//    by NB = 2 column blocks for skinny M (a 32-column strip of B per
+//    workgroup, 256 workgroups at N = 8192), MB = 2 by NB = 1, 2, 4 for
+//    skinny N (a 32-row band of A per workgroup). The small operand is read
+//    by every workgroup and stays in L2.
 //  * Its eight waves split K into eight contiguous ranges of slabs and run
-//    independently: each wave streams its range of the B strip through a
-//    private ring of eight 2 KB LDS stages (buffer -> LDS DMA, seven slabs
-//    ahead), so a CU keeps ~112 KB of B in flight, enough to cover HBM latency
-//    at its 1/256 share of the bandwidth, with no barrier inside the loop.
-//  * A fragments come straight from global memory into registers (each lane's
-//    8 bf16 / 4 fp32 of a row are contiguous), one slab ahead. A and B are
-//    both loaded with inline assembly and waited for with explicit vmcnt
-//    counts (a compiler-visible load would make the compiler's own wait
-//    count drain the B copies in flight every iteration).
+//    independently, with no barrier inside the loop; the partial tiles are
+//    summed through LDS at the end (fixed order: deterministic results).
+//  * Both operands are issued kDepth slabs ahead of the slab being
+//    multiplied: A fragments straight into registers (each lane's 8 bf16 /
+//    4 fp32 of a row are contiguous), rotating through kDepth + 1 register
+//    sets, and B slabs into a private ring of kDepth + 1 LDS stages per wave
+//    (buffer -> LDS DMA). The memory counter retires loads in issue order, so
+//    the two operands run at the same distance: a wait for a nearer A load
+//    would also wait for every B copy issued before it. One slab in flight
+//    per wave (eight per CU) reads HBM fastest here; deeper rings were
+//    measured slower.
+//  * A slab holds KS k blocks of 32 (bf16) or 16 (fp32) k. With KS = 2 a
+//    step reads 128 bytes of each A row, a whole line, instead of half of
+//    one (HBM reads in 64-byte pieces of lines ran at about half the rate of
+//    whole lines in a read-only probe).
+//  * A and B are loaded with inline assembly and waited for with explicit
+//    vmcnt counts (a compiler-visible load would make the compiler's own wait
+//    count drain the copies in flight every slab).
 //  * B fragments are read from the stage with ds_read_b64_tr_b16 (bf16: each
 //    lane gets 8 consecutive k of one column) or ds_read_b32 (fp32), as in the
 //    large-tile kernels; MFMA 16x16x32 bf16 / 16x16x4 f32 with the operands
 //    swapped so a lane's four accumulators are four consecutive columns.
-//  * At the end the eight waves' partial tiles are summed through LDS
-//    (fixed order, so results are deterministic), then bias, activation and
-//    one masked store, as in the other kernels.
+//  * Epilogue: bias, activation and one masked store, as in the other kernels.
 // Requires lda, ldb, ldc, K and N to be multiples of 8 (bf16) or 4 (fp32)
 // and 16-byte aligned pointers.
 #include <type_traits>
@@ -38,177 +48,211 @@ namespace mmrelu {
 namespace {
 
 constexpr int kWaves = 8, kThreads = kWaves * 64;
-constexpr int kBN = 32, kNB = 2;                  // strip width, 16-column blocks per strip
-constexpr int kStages = 8;                         // per-wave ring
-constexpr int kStageBytes = 2048;
-constexpr int kRingBytes = kWaves * kStages * kStageBytes;   // 128 KB
+constexpr int kWaveLdsBytes = 20 * 1024;          // per-wave ring budget (8 waves: 160 KB)
 
 template <typename T>
-struct Skinny;
+struct KBlock;
 template <>
-struct Skinny<uint16_t> {                          // bf16
-    static constexpr int kSlabK = 32;              // k rows per stage (64-byte rows)
-    static constexpr int kRowBytes = kBN * 2;
+struct KBlock<uint16_t> {                          // bf16: 32 k per MFMA
+    static constexpr int kK = 32;
 };
 template <>
-struct Skinny<float> {
-    static constexpr int kSlabK = 16;              // k rows per stage (128-byte rows)
-    static constexpr int kRowBytes = kBN * 4;
+struct KBlock<float> {                             // fp32: 16 k per four MFMAs
+    static constexpr int kK = 16;
 };
 
 // buffer_load_dwordx4 into registers, not visible to the compiler's wait
 // counting (see the file comment); the caller waits explicitly.
-__device__ inline u32x4 load_b128_async(rsrc_t r, uint32_t voffset, uint32_t soffset)
+__device__ inline u32x4 load_b128_async(rsrc_t r, uint32_t voffset)
 {
-    soffset = __builtin_amdgcn_readfirstlane(soffset);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
-    asm("" : "+s"(soffset), "+s"(r));
+    asm("" : "+s"(r));
     u32x4 v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(v) : "v"(voffset), "s"(r), "s"(soffset) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(r) : "memory");
     return v;
 }
 
-template <typename T, int MB>
+// KS k blocks per slab (KS = 2: a row of A read in a step covers a whole
+// 128-byte line); kStages slabs in the ring, kStages - 1 of them in flight.
+template <typename T, int MB, int NB, int KS, int STAGES>
+struct SkinnyShape {
+    static constexpr int kBlkK = KBlock<T>::kK;
+    static constexpr int kSlabK = KS * kBlkK;
+    static constexpr int kEsize = sizeof(T);
+    static constexpr int kRowBytes = 16 * NB * kEsize;             // one k row of the B slab
+    static constexpr int kStageBytes = kSlabK * kRowBytes;         // KS * NB KB
+    static constexpr int kStages = STAGES;
+    static constexpr int kDepth = kStages - 1;                     // slabs in flight ahead
+    static constexpr int kRingBytes = kWaves * kStages * kStageBytes;
+    static constexpr int kRedBytes = kWaves * MB * NB * 64 * 16;   // partial tiles
+    static constexpr int kLdsBytes = kRingBytes > kRedBytes ? kRingBytes : kRedBytes;
+    static_assert(kBlkK * kRowBytes == NB * 1024, "one 1 KB copy per 16 columns and k block");
+    static_assert(kStages >= 2, "ring depth");
+    static_assert(MB * NB <= kWaves, "one reducing wave per 16 x 16 block");
+    static_assert(kDepth * KS * (NB + MB) <= 63, "vmcnt range");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int MB, int NB, int KS, int STAGES>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     const T *__restrict__ A, const T *__restrict__ B, T *__restrict__ C, int M, int N, int K,
     int64_t lda, int64_t ldb, int64_t ldc, const T *__restrict__ bias, int act)
 {
-    using S = Skinny<T>;
-    constexpr int kSlabK = S::kSlabK;
-    constexpr int kEsize = sizeof(T);
-    constexpr int kNBlk = MB * kNB;
-    static_assert(kWaves * kNBlk * 64 * 16 <= kRingBytes, "reduction buffer fits in the ring");
-    static_assert(kSlabK * S::kRowBytes == kStageBytes, "stage size");
-    constexpr int kInFlight = 2 + MB;               // copies and loads issued per iteration
-    static_assert(2 * (kStages - 1) + MB <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRingBytes];
+    using S = SkinnyShape<T, MB, NB, KS, STAGES>;
+    constexpr int kSlabK = S::kSlabK, kBlkK = S::kBlkK, kEsize = S::kEsize, kRowBytes = S::kRowBytes;
+    constexpr int kStageBytes = S::kStageBytes, kStages = S::kStages, kDepth = S::kDepth;
+    constexpr int kSets = kDepth + 1;                  // A register sets = ring stages
+    constexpr int kNBlk = MB * NB;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S::kLdsBytes];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, t = lane & 15;
-    // bf16: consecutive strips on one XCD. A bf16 strip row is 64 bytes, half
-    // of a 128-byte line, and the neighbouring strip reads the other half; on
-    // the same XCD the two share one L2 fill instead of each fetching the
-    // line. An fp32 strip row is a whole line and keeps the dispatch order,
-    // which spreads the strips that run together over more HBM channels
-    // (measured: 8192 x 8192 B at M <= 16 reads 10% faster that way).
-    int n0 = blockIdx.x * kBN;
-    if constexpr (sizeof(T) == 2) {
-        int tm, tn;
-        tile_of(blockIdx.x, gridDim.x, 1, gridDim.x, 1, tm, tn);
-        n0 = tn * kBN;
+
+    // Tile of this workgroup, row-major over the (tiles_m x tiles_n) grid.
+    // bf16 with several column strips: consecutive strips on one XCD. A bf16
+    // 32-column strip row is 64 bytes, half of a 128-byte line, and the
+    // neighbouring strip reads the other half; on the same XCD the two share
+    // one L2 fill instead of each fetching the line. Otherwise the dispatch
+    // order, which spreads the tiles that run together over more HBM channels
+    // (measured: fp32 8192 x 8192 B at M <= 16 reads 10% faster that way).
+    const int tiles_n = (N + 16 * NB - 1) / (16 * NB);
+    int tm, tn;
+    if (sizeof(T) == 2 && tiles_n > 1) {
+        tile_of(blockIdx.x, gridDim.x, (M + 16 * MB - 1) / (16 * MB), tiles_n, 1, tm, tn);
+    } else {
+        tm = blockIdx.x / tiles_n;
+        tn = blockIdx.x % tiles_n;
     }
-    const uint32_t lds0 = lds_address(lds);
-    const uint32_t ring = lds0 + wave * (kStages * kStageBytes);
+    const int m0 = tm * 16 * MB, n0 = tn * 16 * NB;
+    const uint32_t ring = lds_address(lds) + wave * (kStages * kStageBytes);
 
     // This wave's slabs: a contiguous, balanced share of ceil(K / kSlabK).
     const int nk = (K + kSlabK - 1) / kSlabK;
     const int s_begin = (nk * wave) / kWaves, s_end = (nk * (wave + 1)) / kWaves;
     const int n_w = s_end - s_begin;
 
-    // B copies: two 1 KB copies per slab; lane l of copy c fills LDS byte
-    // c*1024 + 16*l of the stage, i.e. row-major rows of kRowBytes.
-    constexpr int kLanesPerRow = S::kRowBytes / 16;
-    uint32_t b_voff[2];
+    // B copies: KS * NB 1 KB copies per slab; lane l of copy c fills LDS byte
+    // c * 1024 + 16 l of the stage, i.e. row-major rows of kRowBytes.
+    constexpr int kCopies = KS * NB;
+    constexpr int kLanesPerRow = kRowBytes / 16;
+    uint32_t b_voff[kCopies];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < kCopies; ++c) {
         const int row = c * (64 / kLanesPerRow) + lane / kLanesPerRow;
         const int col = (lane % kLanesPerRow) * (16 / kEsize);
         b_voff[c] = (n0 + col < N) ? static_cast<uint32_t>((row * ldb + col) * kEsize) : kOutOfRange;
     }
-    auto copy_b = [&](int j) __attribute__((always_inline)) {   // slab j of this wave's range
+    auto copy_b = [&](int j, int stage) __attribute__((always_inline)) {   // slab j of this wave's range
         const int k0 = (s_begin + j) * kSlabK;
         const bool live = j < n_w;
         const rsrc_t rb = make_rsrc(B + static_cast<int64_t>(live ? k0 : 0) * ldb + n0,
                                     live ? ((static_cast<int64_t>(K) - 1 - k0) * ldb + N - n0) * kEsize : 0);
-        const uint32_t st = ring + (j % kStages) * kStageBytes;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) load_to_lds<16>(rb, st + c * 1024, b_voff[c]);
+        for (int c = 0; c < kCopies; ++c) load_to_lds<16>(rb, ring + stage * kStageBytes + c * 1024, b_voff[c]);
     };
 
-    // A loads: block i, lane (g, t) takes row 16i + t and the lane group's k
-    // chunk (bf16: k 8g..8g+7; fp32: k 4g..4g+3) of the slab.
+    // A loads: row block i and k block u of the slab; lane (g, t) takes row
+    // m0 + 16 i + t and the lane group's k chunk of the block (bf16: k 8g..8g+7;
+    // fp32: k 4g..4g+3). The resource is rebased on each slab so every
+    // offset stays small.
     constexpr int kChunkK = 16 / kEsize;
-    const rsrc_t ra = make_rsrc(A, ((static_cast<int64_t>(M) - 1) * lda + K) * kEsize);
     uint32_t a_voff[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
-        a_voff[i] = (16 * i + t < M) ? static_cast<uint32_t>(((16 * i + t) * lda + kChunkK * g) * kEsize) : kOutOfRange;
-    auto load_a = [&](int j, u32x4 (&fa)[MB]) __attribute__((always_inline)) {
+        a_voff[i] = (m0 + 16 * i + t < M) ? static_cast<uint32_t>(((16 * i + t) * lda + kChunkK * g) * kEsize)
+                                          : kOutOfRange;
+    auto load_a = [&](int j, u32x4 (&fa)[KS][MB]) __attribute__((always_inline)) {
         const int k0 = (s_begin + j) * kSlabK;
-        const bool live = j < n_w && k0 + kChunkK * g < K;
+        const bool live = j < n_w;
+        const rsrc_t ra = make_rsrc(A + static_cast<int64_t>(m0) * lda + (live ? k0 : 0),
+                                    live ? ((static_cast<int64_t>(M) - 1 - m0) * lda + K - k0) * kEsize : 0);
 #pragma unroll
-        for (int i = 0; i < MB; ++i) fa[i] = load_b128_async(ra, live ? a_voff[i] : kOutOfRange, live ? k0 * kEsize : 0);
+        for (int u = 0; u < KS; ++u) {
+            const bool in_k = k0 + u * kBlkK + kChunkK * g < K;   // past K the row's padding follows
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                fa[u][i] = load_b128_async(ra, in_k ? a_voff[i] + u * kBlkK * kEsize : kOutOfRange);
+        }
     };
 
-    f32x4 acc[MB][kNB];
+    f32x4 acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One slab: B fragments from the stage, MFMAs with the A fragments.
-    auto compute = [&](int j, const u32x4 (&fa)[MB]) __attribute__((always_inline)) {
-        const uint8_t *st = lds + wave * (kStages * kStageBytes) + (j % kStages) * kStageBytes;
-        if constexpr (std::is_same_v<T, uint16_t>) {
+    auto compute = [&](int stage, const u32x4 (&fa)[KS][MB]) __attribute__((always_inline)) {
+        const uint8_t *st = lds + wave * (kStages * kStageBytes) + stage * kStageBytes;
 #pragma unroll
-            for (int jb = 0; jb < kNB; ++jb) {
-                i16x4 half[2];
+        for (int u = 0; u < KS; ++u) {
+            const uint8_t *sb = st + u * kBlkK * kRowBytes;
+            if constexpr (std::is_same_v<T, uint16_t>) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 8 * g + 4 * h + (t >> 2);
-                    const int col = 16 * jb + 4 * (t & 3);
-                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (MMRELU_LDS i16x4 *)(st + row * S::kRowBytes + col * 2));
-                }
-                const bf16x8 fb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int jb = 0; jb < NB; ++jb) {
+                    i16x4 half[2];
 #pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, __builtin_bit_cast(bf16x8, fa[i]), acc[i][jb], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int jb = 0; jb < kNB; ++jb) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float b = *reinterpret_cast<const float *>(st + (4 * g + s) * S::kRowBytes + (16 * jb + t) * 4);
+                    for (int h = 0; h < 2; ++h) {
+                        const int row = 8 * g + 4 * h + (t >> 2);
+                        const int col = 16 * jb + 4 * (t & 3);
+                        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (MMRELU_LDS i16x4 *)(sb + row * kRowBytes + col * 2));
+                    }
+                    const bf16x8 fb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                     for (int i = 0; i < MB; ++i)
-                        acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, __uint_as_float(fa[i][s]), acc[i][jb], 0, 0, 0);
+                        acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, __builtin_bit_cast(bf16x8, fa[u][i]), acc[i][jb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float b = *reinterpret_cast<const float *>(sb + (4 * g + s) * kRowBytes + (16 * jb + t) * 4);
+#pragma unroll
+                        for (int i = 0; i < MB; ++i)
+                            acc[i][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, __uint_as_float(fa[u][i][s]), acc[i][jb], 0, 0, 0);
+                    }
                 }
             }
         }
     };
 
-    // Pipeline: slabs 0 .. kStages-2 copied and slab 0's A loaded up front.
-    // Step j issues the copy of slab j+kStages-1 into the stage slab j-1 used
-    // (read and consumed in step j-1), then A of slab j+1, then waits until
-    // everything issued before this step has landed (slab j's A, and its B
-    // copy, issued earlier), and multiplies slab j. Copies and loads past the
-    // wave's range are fully masked, so every step issues the same count.
-    // Two A register sets alternate (the loop is unrolled by two): a load
-    // lands in the set the following step reads after its wait. Copying a
-    // register whose load is still in flight would read stale data, so no
-    // step moves one set into the other.
-    u32x4 fa0[MB], fa1[MB];
-    auto step = [&](int j, u32x4 (&cur)[MB], u32x4 (&next)[MB]) __attribute__((always_inline)) {
+    // Pipeline: slabs 0 .. kDepth-1 issued up front (B copy, then A load).
+    // Step j issues slab j + kDepth into the ring stage and register set that
+    // slab j - 1 used (read and consumed in step j - 1), then waits until
+    // everything issued before slab j + 1 has landed, i.e. slab j itself, and
+    // multiplies slab j. Slab j lives in stage and set j mod kSets; the loop
+    // is unrolled by kSets so both are compile-time constants (a runtime
+    // index would put the register sets in scratch), and no set is ever
+    // copied into another: a copy of a register whose load is still in flight
+    // would read stale data. Copies and loads past the wave's range are fully
+    // masked, so every step issues the same count.
+    u32x4 fa[kSets][KS][MB];
+    auto step = [&](int j, int q) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        copy_b(j + kStages - 1);
-        load_a(j + 1, next);
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kInFlight) : "memory");
+        copy_b(j + kDepth, (q + kDepth) % kSets);
+        load_a(j + kDepth, fa[(q + kDepth) % kSets]);
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDepth * KS * (NB + MB)) : "memory");
 #pragma unroll
-        for (int i = 0; i < MB; ++i) asm volatile("" : "+v"(cur[i]));
+        for (int u = 0; u < KS; ++u)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) asm volatile("" : "+v"(fa[q][u][i]));
         __builtin_amdgcn_sched_barrier(0);
-        compute(j, cur);
+        compute(q, fa[q]);
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
-    for (int j = 0; j + 1 < kStages; ++j) copy_b(j);
-    load_a(0, fa0);
-    for (int j = 0; j < n_w; j += 2) {
-        step(j, fa0, fa1);
-        if (j + 1 < n_w) step(j + 1, fa1, fa0);
+    for (int q = 0; q < kDepth; ++q) {
+        copy_b(q, q);
+        load_a(q, fa[q]);
+    }
+    for (int j0 = 0; j0 < n_w; j0 += kSets) {
+#pragma unroll
+        for (int q = 0; q < kSets; ++q)
+            if (j0 + q < n_w) step(j0 + q, q);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -220,14 +264,14 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int jb = 0; jb < kNB; ++jb) red[(wave * kNBlk + i * kNB + jb) * 64 + lane] = acc[i][jb];
+        for (int jb = 0; jb < NB; ++jb) red[(wave * kNBlk + i * NB + jb) * 64 + lane] = acc[i][jb];
     __syncthreads();
     if (wave >= kNBlk) return;
     f32x4 v = red[wave * 64 + lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) v += red[(w * kNBlk + wave) * 64 + lane];
-    const int i = wave / kNB, jb = wave % kNB;
-    const int row = 16 * i + t;
+    const int i = wave / NB, jb = wave % NB;
+    const int row = 16 * i + t;                        // within the tile
     const int col = 16 * jb + 4 * g;
 
     // Epilogue: bias of the lane's four columns (only when there is one),
@@ -242,8 +286,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
 #pragma unroll
         for (int r = 0; r < 4; ++r) bj[r] = 0.0f;
     }
-    const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + n0, ((static_cast<int64_t>(M) - 1) * ldc + N - n0) * kEsize);
-    const uint32_t off = (row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * kEsize) : kOutOfRange;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0, ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * kEsize);
+    const uint32_t off = (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * kEsize) : kOutOfRange;
     with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
         constexpr int ACT = decltype(act_c)::value;
         if constexpr (std::is_same_v<T, uint16_t>) {
@@ -260,10 +305,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     });
 }
 
-template <typename T, int MB>
+template <typename T, int MB, int NB, int KS, int STAGES>
 hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mmrelu_skinny<T, MB>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((mmrelu_skinny<T, MB, NB, KS, STAGES>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const T *>(p.A), static_cast<const T *>(p.B), static_cast<T *>(p.C), p.M, p.N,
                        p.K, p.lda, p.ldb, p.ldc, static_cast<const T *>(p.bias), p.act);
     return hipGetLastError();
@@ -271,27 +316,48 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 
 }  // namespace
 
-// block_m is the most rows a variant covers; the planner picks the smallest
-// that holds M. wg_per_cu 1 (128 KB of LDS per workgroup).
-const Variant *variant_f32_skinny(int mb)
+// Skinny-M tiles (16, 32 or 64 rows by 32 columns) and skinny-N tiles (32
+// rows by 16, 32 or 64 columns). Any shape is covered by a grid of tiles;
+// the planner uses them where one dimension is small. Each uses the k depth
+// per slab (KS) and ring depth measured fastest for its role at 8192 x 8192:
+// two stages (one slab in flight) throughout, since deeper rings read HBM
+// more slowly here (fp32 1 x 8192 x 8192: 39 us with two stages, 48 us with
+// eight); KS = 2 where the rows of the streamed operand would otherwise be
+// read as half lines (skinny N, and fp32 at 64 rows). wg_per_cu 1.
+const Variant *variant_f32_skinny(int mb, int nb, int ks)
 {
-    static const Variant v1 = {"mmrelu_skinny<float,16x32>", MMRELU_DTYPE_F32, 16, kBN, 16, kThreads, 1, 4,
-                               launch_skinny<float, 1>, 1.0f, 16};
-    static const Variant v2 = {"mmrelu_skinny<float,32x32>", MMRELU_DTYPE_F32, 32, kBN, 16, kThreads, 1, 4,
-                               launch_skinny<float, 2>, 1.0f, 32};
-    static const Variant v4 = {"mmrelu_skinny<float,64x32>", MMRELU_DTYPE_F32, 64, kBN, 16, kThreads, 1, 4,
-                               launch_skinny<float, 4>, 1.0f, 64};
-    return mb == 1 ? &v1 : mb == 2 ? &v2 : &v4;
+    static const Variant m1 = {"mmrelu_skinny<float,16x32,ks1>", MMRELU_DTYPE_F32, 16, 32, 16, kThreads, 1, 4,
+                               launch_skinny<float, 1, 2, 1, 2>, 1.0f};
+    static const Variant m2 = {"mmrelu_skinny<float,32x32,ks1>", MMRELU_DTYPE_F32, 32, 32, 16, kThreads, 1, 4,
+                               launch_skinny<float, 2, 2, 1, 2>, 1.0f};
+    static const Variant m4 = {"mmrelu_skinny<float,64x32,ks2>", MMRELU_DTYPE_F32, 64, 32, 32, kThreads, 1, 4,
+                               launch_skinny<float, 4, 2, 2, 2>, 1.0f};
+    static const Variant n1 = {"mmrelu_skinny<float,32x16,ks2>", MMRELU_DTYPE_F32, 32, 16, 32, kThreads, 1, 4,
+                               launch_skinny<float, 2, 1, 2, 2>, 1.0f};
+    static const Variant n2 = {"mmrelu_skinny<float,32x32,ks2>", MMRELU_DTYPE_F32, 32, 32, 32, kThreads, 1, 4,
+                               launch_skinny<float, 2, 2, 2, 2>, 1.0f};
+    static const Variant n4 = {"mmrelu_skinny<float,32x64,ks2>", MMRELU_DTYPE_F32, 32, 64, 32, kThreads, 1, 4,
+                               launch_skinny<float, 2, 4, 2, 2>, 1.0f};
+    if (nb == 2 && ks == 1) return mb == 1 ? &m1 : &m2;
+    if (nb == 2 && mb == 4) return &m4;
+    return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
 }
-const Variant *variant_bf16_skinny(int mb)
+const Variant *variant_bf16_skinny(int mb, int nb, int ks)
 {
-    static const Variant v1 = {"mmrelu_skinny<bf16,16x32>", MMRELU_DTYPE_BF16, 16, kBN, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 1>, 1.0f, 16};
-    static const Variant v2 = {"mmrelu_skinny<bf16,32x32>", MMRELU_DTYPE_BF16, 32, kBN, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2>, 1.0f, 32};
-    static const Variant v4 = {"mmrelu_skinny<bf16,64x32>", MMRELU_DTYPE_BF16, 64, kBN, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 4>, 1.0f, 64};
-    return mb == 1 ? &v1 : mb == 2 ? &v2 : &v4;
+    static const Variant m1 = {"mmrelu_skinny<bf16,16x32,ks1>", MMRELU_DTYPE_BF16, 16, 32, 32, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 1, 2, 1, 2>, 1.0f};
+    static const Variant m2 = {"mmrelu_skinny<bf16,32x32,ks1>", MMRELU_DTYPE_BF16, 32, 32, 32, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 2, 2, 1, 2>, 1.0f};
+    static const Variant m4 = {"mmrelu_skinny<bf16,64x32,ks1>", MMRELU_DTYPE_BF16, 64, 32, 32, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 4, 2, 1, 2>, 1.0f};
+    static const Variant n1 = {"mmrelu_skinny<bf16,32x16,ks2>", MMRELU_DTYPE_BF16, 32, 16, 64, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 2, 1, 2, 2>, 1.0f};
+    static const Variant n2 = {"mmrelu_skinny<bf16,32x32,ks2>", MMRELU_DTYPE_BF16, 32, 32, 64, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 2, 2, 2, 2>, 1.0f};
+    static const Variant n4 = {"mmrelu_skinny<bf16,32x64,ks2>", MMRELU_DTYPE_BF16, 32, 64, 64, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 2, 4, 2, 2>, 1.0f};
+    if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;
+    return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
 }
 
 }  // namespace mmrelu

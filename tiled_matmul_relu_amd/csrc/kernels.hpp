@@ -33,9 +33,6 @@ struct Variant {
     // Measured time per output element of a full tile, relative to the
     // dtype's fastest kernel (the planner's cost model).
     float rel_cost = 1.0f;
-    // Most rows of C the kernel covers (0: any M; the skinny kernels cover
-    // one row strip of block_m rows).
-    int max_m = 0;
 };
 
 // Kernel variants, defined in the kernel translation units (host functions
@@ -50,8 +47,11 @@ const Variant *variant_bf16_mfma256();
 const Variant *variant_bf16_mfma256_8w();
 const Variant *variant_bf16_pingpong256();
 const Variant *variant_bf16_mfma128();
-// Skinny-M kernels (k_skinny.hip): mb = 1, 2 or 4 covers M <= 16 * mb.
-const Variant *variant_f32_skinny(int mb);
-const Variant *variant_bf16_skinny(int mb);
+// Skinny kernels (k_skinny.hip), tiles of 16 mb x 16 nb with K split over
+// the eight waves and ks k blocks per slab: (mb, nb, ks) = (1, 2, 1),
+// (2, 2, 1), (4, 2, 2 for fp32 / 1 for bf16) for skinny M and (2, 1, 2),
+// (2, 2, 2), (2, 4, 2) for skinny N.
+const Variant *variant_f32_skinny(int mb, int nb, int ks);
+const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 
 }  // namespace mmrelu

@@ -15,22 +15,26 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 8;
-constexpr int kNumBf16 = 8;
+constexpr int kNumF32 = 11;
+constexpr int kNumBf16 = 11;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
                                               variant_f32_mfma128_unaligned(), variant_f32_mfma64(),
-                                              variant_f32_mfma64_unaligned(), variant_f32_skinny(1),
-                                              variant_f32_skinny(2), variant_f32_skinny(4)};
+                                              variant_f32_mfma64_unaligned(), variant_f32_skinny(1, 2, 1),
+                                              variant_f32_skinny(2, 2, 1), variant_f32_skinny(4, 2, 2),
+                                              variant_f32_skinny(2, 1, 2), variant_f32_skinny(2, 2, 2),
+                                              variant_f32_skinny(2, 4, 2)};
     return t;
 }
 const Variant *const *bf16_table()
 {
     static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256(),
                                                variant_bf16_mfma256_8w(), variant_bf16_pingpong256(),
-                                               variant_bf16_mfma128(), variant_bf16_skinny(1),
-                                               variant_bf16_skinny(2), variant_bf16_skinny(4)};
+                                               variant_bf16_mfma128(), variant_bf16_skinny(1, 2, 1),
+                                               variant_bf16_skinny(2, 2, 1), variant_bf16_skinny(4, 2, 1),
+                                               variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
+                                               variant_bf16_skinny(2, 4, 2)};
     return t;
 }
 
@@ -110,11 +114,16 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {3, 4};
     const Variant *const *table = dtype == MMRELU_DTYPE_F32 ? f32_table() : bf16_table();
     const bool fits = layout_fits(table[dtype == MMRELU_DTYPE_F32 ? 1 : 3], N, K, lda, ldb, ldc, A, B, C);
-    // Skinny M (<= 64 rows): the product is bound by reading B once, and the
-    // skinny kernels spread that read over one workgroup per 32 columns with
-    // K split across eight waves (variants 5, 6, 7: up to 16, 32, 64 rows).
-    if (fits && M <= 64) {
-        const int32_t v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
+    // Skinny M or N (<= 64): the product is bound by reading the large
+    // operand once, and the skinny kernels spread that read over one
+    // workgroup per 32 columns of B (skinny M: variants 5, 6, 7 for up to 16,
+    // 32, 64 rows) or per 32 rows of A (skinny N: variants 8, 9, 10 for up to
+    // 16, 32, 64 columns), with K split across eight waves. When both are
+    // small, the smaller one decides.
+    if (fits && (M <= 64 || N <= 64)) {
+        int32_t v;
+        if (M <= 64 && M <= N) v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
+        else v = N <= 16 ? 8 : N <= 32 ? 9 : 10;
         if (layout_fits(table[v], N, K, lda, ldb, ldc, A, B, C)) return v;
     }
     const int32_t *cand = nullptr;
@@ -176,7 +185,6 @@ int run(int dtype, int32_t variant, int act, const void *A, const void *B, const
     const Variant *v = variant_at(dtype, variant);
     if (v == nullptr) return MMRELU_ERR_INVALID_VALUE;
     if (K > 0 && !layout_fits(v, N, K, lda, ldb, ldc, A, B, C)) return MMRELU_ERR_INVALID_VALUE;
-    if (v->max_m > 0 && M > v->max_m) return MMRELU_ERR_INVALID_VALUE;
     if (M == 0 || N == 0) return MMRELU_OK;
     mmrelu_plan_t plan;
     rc = fill_plan(v, variant, M, N, kDefaultCus, &plan);
