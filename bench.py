@@ -66,6 +66,37 @@ def read_counters(path, counter):
     return out
 
 
+def calibrated_counters(fetch_csv, write_csv, calib_mib):
+    """FETCH_SIZE and WRITE_SIZE per kernel name (KiB per dispatch, lists),
+    and the factors that turn them into bytes: each counter is scaled by what
+    it reads for the calibration copy of calib_mib MiB in the same run, whose
+    true traffic is calib_mib MiB read and calib_mib MiB written."""
+    fetch = read_counters(fetch_csv, "FETCH_SIZE")
+    write = read_counters(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if len(copy) != 1 or copy[0] not in write:
+        raise SystemExit(f"counters: expected one copy kernel in the counter files, found {copy}")
+    # The calibration copy is the largest copy dispatch of the run (inputs
+    # may also be staged through small copy kernels).
+    calib = calib_mib * (1 << 20)
+    return fetch, write, calib / (max(fetch[copy[0]]) * 1024), calib / (max(write[copy[0]]) * 1024)
+
+
+def counter_summary(fetch_csv, write_csv, calib_mib):
+    """One JSON line per mmrelu kernel in two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE) of the same command: calibrated HBM bytes read and written
+    per dispatch (mean over its dispatches)."""
+    fetch, write, f_fac, w_fac = calibrated_counters(fetch_csv, write_csv, calib_mib)
+    for name in sorted(fetch):
+        if "mmrelu" not in name or name not in write:
+            continue
+        fv, wv = fetch[name], write[name]
+        print(json.dumps({"kernel_symbol": name.split(">(")[0] + ">", "dispatches": min(len(fv), len(wv)),
+                          "fetch_bytes": round(sum(fv) / len(fv) * 1024 * f_fac),
+                          "write_bytes": round(sum(wv) / len(wv) * 1024 * w_fac),
+                          "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4)}))
+
+
 def record_traffic(fetch_csv, write_csv, calib_mib, command):
     """Write profiles/traffic.json from two rocprofv3 --pmc runs of this script
     (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch) that included the
@@ -74,14 +105,7 @@ def record_traffic(fetch_csv, write_csv, calib_mib, command):
     calib_mib MiB written."""
     import datagen
     import tiled_matmul_relu_amd as mm
-    fetch = read_counters(fetch_csv, "FETCH_SIZE")
-    write = read_counters(write_csv, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k]
-    if len(copy) != 1 or copy[0] not in write:
-        raise SystemExit(f"record-traffic: expected one copy kernel in the counter files, found {copy}")
-    calib = calib_mib * (1 << 20)
-    f_fac = calib / (fetch[copy[0]][-1] * 1024)
-    w_fac = calib / (write[copy[0]][-1] * 1024)
+    fetch, write, f_fac, w_fac = calibrated_counters(fetch_csv, write_csv, calib_mib)
     recs = {}
     for kind, cid in (("bf16", 5), ("f32", 3)):
         cfg = datagen.CONFIGS[cid]
@@ -114,6 +138,18 @@ def record_traffic(fetch_csv, write_csv, calib_mib, command):
         json.dump(recs, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(recs, indent=1, sort_keys=True))
+
+
+def calib_copy(mib, torch):
+    """One device-to-device copy of mib MiB (a kernel of known traffic, for
+    scaling memory counters); returns the bytes copied."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n * 4
 
 
 def to_device(x, torch):
@@ -185,6 +221,16 @@ def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="re
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    # Back-to-back: the same calls with no event between them, so the
+    # queue never waits for an event packet (the per-call times carry a
+    # few microseconds of that gap, which matters for short kernels).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b = e0.elapsed_time(e1) / steps
     mean = sum(t) / steps
     med = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
     p95 = t[min(steps - 1, int(math.ceil(0.95 * steps)) - 1)]
@@ -197,7 +243,8 @@ def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="re
             "idle_slots_last_wave": plan["idle_slots_last"], "steps": steps, "warmup": warmup,
             "mean_ms": round(mean, 5), "median_ms": round(med, 5), "p95_ms": round(p95, 5),
             "tflops_median": round(tf, 3), "pct_of_peak": round(100 * tf / PEAK_TFLOPS[cfg.dtype], 2),
-            "alg_gbs_median": round(alg_bytes / (med * 1e-3) / 1e9, 1)}
+            "alg_gbs_median": round(alg_bytes / (med * 1e-3) / 1e9, 1),
+            "b2b_ms": round(b2b, 5), "alg_gbs_b2b": round(alg_bytes / (b2b * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(cfg, a, b, target_s, oracle):
@@ -243,6 +290,14 @@ def main():
                     help="instead of the benchmark line: square sizes 256..8192 and skinny shapes (M or N of "
                          "1..64, the others 8192) in both dtypes, per-call statistics with the bounding roofline "
                          "(MFMA or HBM) and the fraction of it reached, one JSON line each")
+    ap.add_argument("--shapes", default="",
+                    help="with --sweep: only these shapes, comma-separated dtype:MxNxK (e.g. f32:1x8192x8192)")
+    ap.add_argument("--sweep-steps", type=int, default=0,
+                    help="with --sweep: timed calls per shape (default 100, 40 above 2e11 FLOPs)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: calibrated HBM bytes per dispatch of each mmrelu kernel in the "
+                         "counter_collection.csv files of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "command run with --calib-copy-mib, one JSON line each")
     ap.add_argument("--act", choices=["relu", "gelu_tanh", "none"], default="relu",
                     help="with --all-configs: the fused epilogue's activation")
     ap.add_argument("--bias", action="store_true", help="with --all-configs: add a per-column bias")
@@ -270,20 +325,36 @@ def main():
             print("bench.py: no GPU visible", file=sys.stderr)
             sys.exit(1)
         mm.load_library()
+        if args.calib_copy_mib > 0:
+            calib_copy(args.calib_copy_mib, torch)
+        todo = []
         for dtype in ("f32", "bf16"):
             shapes = [(n, n, n) for n in (256, 512, 1024, 2048, 4096, 8192)]
             shapes += [(m, 8192, 8192) for m in (1, 8, 16, 32, 64)] + [(8192, n, 8192) for n in (1, 16, 64)]
-            for (M, N, K) in shapes:
-                cfg = datagen.Config(0, f"{dtype}_{M}x{N}x{K}", dtype, M, N, K, K, N, N, "normal_over_sqrtk")
-                steps = 40 if cfg.flops > 2e11 else 100
-                r = per_call_stats(cfg, steps, 20, torch, mm, datagen)
-                peak = PEAK_TFLOPS[dtype]
-                t_mfma = cfg.flops / (peak * 1e12) * 1e3
-                t_hbm = cfg.elem_bytes * (M * K + K * N + M * N) / (HBM_PEAK_GBS * 1e9) * 1e3
-                r["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
-                r["roofline_frac"] = round(max(t_mfma, t_hbm) / r["median_ms"], 4)
-                r["pct_of_hbm_peak"] = round(100 * r["alg_gbs_median"] / HBM_PEAK_GBS, 2)
-                print(json.dumps(r), flush=True)
+            todo += [(dtype, s) for s in shapes]
+        if args.shapes:
+            todo = []
+            for item in args.shapes.split(","):
+                dtype, dims = item.split(":")
+                todo.append((dtype, tuple(int(x) for x in dims.split("x"))))
+        for dtype, (M, N, K) in todo:
+            cfg = datagen.Config(0, f"{dtype}_{M}x{N}x{K}", dtype, M, N, K, K, N, N, "normal_over_sqrtk")
+            steps = args.sweep_steps or (40 if cfg.flops > 2e11 else 100)
+            r = per_call_stats(cfg, steps, 20, torch, mm, datagen)
+            peak = PEAK_TFLOPS[dtype]
+            t_mfma = cfg.flops / (peak * 1e12) * 1e3
+            t_hbm = cfg.elem_bytes * (M * K + K * N + M * N) / (HBM_PEAK_GBS * 1e9) * 1e3
+            r["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+            r["roofline_frac"] = round(max(t_mfma, t_hbm) / r["median_ms"], 4)
+            r["pct_of_hbm_peak"] = round(100 * r["alg_gbs_median"] / HBM_PEAK_GBS, 2)
+            r["roofline_frac_b2b"] = round(max(t_mfma, t_hbm) / r["b2b_ms"], 4)
+            print(json.dumps(r), flush=True)
+        return
+
+    if args.counter_summary:
+        if args.calib_copy_mib <= 0:
+            ap.error("--counter-summary needs --calib-copy-mib (the size the profiled runs copied)")
+        counter_summary(args.counter_summary[0], args.counter_summary[1], args.calib_copy_mib)
         return
 
     if args.record_traffic:
@@ -349,13 +420,7 @@ def main():
                             "kernel": r32["plan"]["name"],
                             "traffic": measured_traffic("f32", r32["plan"]["name"])}
     if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["calib_copy_bytes"] = n * 4
+        out["calib_copy_bytes"] = calib_copy(args.calib_copy_mib, torch)
     if not args.no_cpu_baseline:
         import oracle
         a, b = res["inputs"]
