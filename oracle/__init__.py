@@ -7,9 +7,10 @@ shares no code with it; this package does not import the library either.
 The arithmetic lives in ``mmrelu_oracle.c`` (plain C, OpenMP over rows),
 built with gcc into ``liboracle.so`` next to it. Each routine is the plain
 definition R[i][j] = max(0, sum_k A[i][k]·B[k][j]) in fp64 with ascending k,
-and its fused-epilogue form R[i][j] = act(sum_k A[i][k]·B[k][j] + bias[j])
-with act one of ReLU, GeLU (tanh form) or none; see the C file for the
-passages it follows.
+its fused-epilogue form R[i][j] = act(sum_k A[i][k]·B[k][j] + bias[j])
+with act one of ReLU, GeLU (tanh form) or none, and its general-stride form
+(A[i][k] = a[i*sam + k*sak], B[k][j] = b[k*sbk + j*sbn]); see the C file for
+the passages it follows.
 """
 from __future__ import annotations
 
@@ -58,6 +59,14 @@ def _load():
     for name in ("oracle_fused_f32_at", "oracle_fused_bf16_at"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, p, p, i64, p]
+        fn.restype = None
+    for name in ("oracle_strided_f32", "oracle_strided_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_strided_f32_at", "oracle_strided_bf16_at"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, i64, i64, p, p, i64, p]
         fn.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -182,5 +191,57 @@ def fused_at(act: str, a: np.ndarray, b: np.ndarray, bias, rows, cols, K: int, l
     if ii.size:
         fn = "oracle_fused_f32_at" if dtype == np.float32 else "oracle_fused_bf16_at"
         getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, K, lda, ldb,
+                             ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
+    return out
+
+
+def _check_strided(a, b, M, N, K, sam, sak, sbk, sbn):
+    dtype, _, _ = _dtype_and_fns(a)
+    if b.dtype != dtype:
+        raise TypeError("a and b differ in dtype")
+    if not (a.flags.c_contiguous and b.flags.c_contiguous):
+        raise ValueError("oracle inputs must be C-contiguous buffers")
+    if min(M, N, K) < 0 or min(sam, sak, sbk, sbn) < 0:
+        raise ValueError("negative size or stride")
+    if M > 0 and K > 0 and a.size <= (M - 1) * sam + (K - 1) * sak:
+        raise ValueError("A buffer too small for its strides")
+    if K > 0 and N > 0 and b.size <= (K - 1) * sbk + (N - 1) * sbn:
+        raise ValueError("B buffer too small for its strides")
+    return dtype
+
+
+def strided(act: str, a: np.ndarray, b: np.ndarray, bias, M: int, N: int, K: int,
+            sam: int, sak: int, sbk: int, sbn: int) -> np.ndarray:
+    """act(A·B + bias) as an M x N float64 array, with A[i][k] = a.flat[i*sam +
+    k*sak] and B[k][j] = b.flat[k*sbk + j*sbn] (non-negative strides, in
+    elements); ``a``/``b`` are C-contiguous float32 or uint16 (bf16) buffers."""
+    dtype = _check_strided(a, b, M, N, K, sam, sak, sbk, sbn)
+    bp = _bias_ptr(bias, dtype, N)
+    r = np.empty((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return r
+    fn = "oracle_strided_f32" if dtype == np.float32 else "oracle_strided_bf16"
+    rc = getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, r.ctypes.data, M, N, K,
+                              sam, sak, sbk, sbn, N)
+    if rc != 0:
+        raise MemoryError("oracle could not allocate its row accumulator")
+    return r
+
+
+def strided_at(act: str, a: np.ndarray, b: np.ndarray, bias, rows, cols, M: int, N: int, K: int,
+               sam: int, sak: int, sbk: int, sbn: int) -> np.ndarray:
+    """act(A·B + bias)[rows[t], cols[t]] for each t with general strides, as float64."""
+    dtype = _check_strided(a, b, M, N, K, sam, sak, sbk, sbn)
+    ii = np.ascontiguousarray(rows, dtype=np.int64)
+    jj = np.ascontiguousarray(cols, dtype=np.int64)
+    if ii.shape != jj.shape:
+        raise ValueError("rows and cols differ in length")
+    if ii.size and (ii.min() < 0 or jj.min() < 0 or ii.max() >= M or jj.max() >= N):
+        raise ValueError("index outside the M x N result")
+    bp = _bias_ptr(bias, dtype, N)
+    out = np.empty(ii.size, dtype=np.float64)
+    if ii.size:
+        fn = "oracle_strided_f32_at" if dtype == np.float32 else "oracle_strided_bf16_at"
+        getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, K, sam, sak, sbk, sbn,
                              ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
     return out

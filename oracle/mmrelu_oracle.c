@@ -47,6 +47,20 @@
  *                                none(x)  = x
  *
  * with the pages' constants and libm's tanh, all in double.
+ *
+ * General strides (the "oracle_strided_*" routines; every other routine is
+ * the case of unit column strides). The lecture reminds that a tensor is
+ * linearised in memory and that its strides map a (row, column) index to a
+ * position, row times the row stride plus column times the column stride,
+ * a transpose being the same data with the two strides exchanged (section
+ * "Reductions and tiling", before the matmul kernel); the Chinese notes'
+ * section 5.5 kernel takes one stride per dimension of A, B and C. So
+ *
+ *     A[i][k] = A[i*sam + k*sak],   B[k][j] = B[k*sbk + j*sbn]
+ *
+ * with any non-negative strides (zero repeats an element), and the result is
+ * the same act(sum + bias) as above, stored row-major in R (ld ldr): where C
+ * lives is the library's concern, the values are the oracle's.
  */
 #include <math.h>
 #include <stdint.h>
@@ -88,11 +102,12 @@ int oracle_num_threads(void)
 #endif
 }
 
-/* Full act(A·B + bias) for fp32 inputs into a double M x N matrix R (ld
- * ldr); bias is N floats or NULL. Returns 0, or -1 if a row accumulator
- * could not be allocated. */
-int oracle_fused_f32(int act, const float *A, const float *B, const float *bias, double *R,
-                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
+/* Full act(A·B + bias) for fp32 inputs with general strides into a double
+ * M x N matrix R (ld ldr); bias is N floats or NULL. Returns 0, or -1 if a row
+ * accumulator could not be allocated. */
+int oracle_strided_f32(int act, const float *A, const float *B, const float *bias, double *R,
+                       int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk,
+                       int64_t sbn, int64_t ldr)
 {
     int failed = 0;
 #pragma omp parallel
@@ -107,9 +122,9 @@ int oracle_fused_f32(int act, const float *A, const float *B, const float *bias,
             if (!acc) continue;
             for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                const double a = (double)A[i * lda + k];
-                const float *brow = B + k * ldb;
-                for (int64_t j = 0; j < N; ++j) acc[j] += a * (double)brow[j];
+                const double a = (double)A[i * sam + k * sak];
+                const float *brow = B + k * sbk;
+                for (int64_t j = 0; j < N; ++j) acc[j] += a * (double)brow[j * sbn];
             }
             for (int64_t j = 0; j < N; ++j)
                 R[i * ldr + j] = activate(act, acc[j] + (bias ? (double)bias[j] : 0.0));
@@ -120,8 +135,9 @@ int oracle_fused_f32(int act, const float *A, const float *B, const float *bias,
 }
 
 /* Same for bf16 inputs and bias given as uint16 bit patterns. */
-int oracle_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, double *R,
-                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
+int oracle_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, double *R,
+                        int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk,
+                        int64_t sbn, int64_t ldr)
 {
     int failed = 0;
 #pragma omp parallel
@@ -136,9 +152,9 @@ int oracle_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint1
             if (!acc) continue;
             for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
             for (int64_t k = 0; k < K; ++k) {
-                const double a = widen_bf16(A[i * lda + k]);
-                const uint16_t *brow = B + k * ldb;
-                for (int64_t j = 0; j < N; ++j) acc[j] += a * widen_bf16(brow[j]);
+                const double a = widen_bf16(A[i * sam + k * sak]);
+                const uint16_t *brow = B + k * sbk;
+                for (int64_t j = 0; j < N; ++j) acc[j] += a * widen_bf16(brow[j * sbn]);
             }
             for (int64_t j = 0; j < N; ++j)
                 R[i * ldr + j] = activate(act, acc[j] + (bias ? widen_bf16(bias[j]) : 0.0));
@@ -149,30 +165,57 @@ int oracle_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint1
 }
 
 /* Entries R[ii[t]][jj[t]] for t < n, each as one dot product in ascending k. */
-void oracle_fused_f32_at(int act, const float *A, const float *B, const float *bias, int64_t K,
-                         int64_t lda, int64_t ldb,
-                         const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+void oracle_strided_f32_at(int act, const float *A, const float *B, const float *bias, int64_t K,
+                           int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
+                           const int64_t *ii, const int64_t *jj, int64_t n, double *out)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < n; ++t) {
         double s = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            s += (double)A[ii[t] * lda + k] * (double)B[k * ldb + jj[t]];
+            s += (double)A[ii[t] * sam + k * sak] * (double)B[k * sbk + jj[t] * sbn];
         out[t] = activate(act, s + (bias ? (double)bias[jj[t]] : 0.0));
     }
+}
+
+void oracle_strided_bf16_at(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, int64_t K,
+                            int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
+                            const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += widen_bf16(A[ii[t] * sam + k * sak]) * widen_bf16(B[k * sbk + jj[t] * sbn]);
+        out[t] = activate(act, s + (bias ? widen_bf16(bias[jj[t]]) : 0.0));
+    }
+}
+
+/* Row-major operands with leading dimensions: unit column strides. */
+int oracle_fused_f32(int act, const float *A, const float *B, const float *bias, double *R,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
+{
+    return oracle_strided_f32(act, A, B, bias, R, M, N, K, lda, 1, ldb, 1, ldr);
+}
+
+int oracle_fused_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, double *R,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldr)
+{
+    return oracle_strided_bf16(act, A, B, bias, R, M, N, K, lda, 1, ldb, 1, ldr);
+}
+
+void oracle_fused_f32_at(int act, const float *A, const float *B, const float *bias, int64_t K,
+                         int64_t lda, int64_t ldb,
+                         const int64_t *ii, const int64_t *jj, int64_t n, double *out)
+{
+    oracle_strided_f32_at(act, A, B, bias, K, lda, 1, ldb, 1, ii, jj, n, out);
 }
 
 void oracle_fused_bf16_at(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, int64_t K,
                           int64_t lda, int64_t ldb,
                           const int64_t *ii, const int64_t *jj, int64_t n, double *out)
 {
-#pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < n; ++t) {
-        double s = 0.0;
-        for (int64_t k = 0; k < K; ++k)
-            s += widen_bf16(A[ii[t] * lda + k]) * widen_bf16(B[k * ldb + jj[t]]);
-        out[t] = activate(act, s + (bias ? widen_bf16(bias[jj[t]]) : 0.0));
-    }
+    oracle_strided_bf16_at(act, A, B, bias, K, lda, 1, ldb, 1, ii, jj, n, out);
 }
 
 /* relu(A·B): the fused routines with ReLU and no bias. */
