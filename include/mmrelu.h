@@ -16,7 +16,8 @@
  * column strides to 1, the row-major case).
  *
  * Ownership and execution: all pointers are DEVICE pointers owned by the
- * caller; the library never allocates, frees, or synchronises. The caller
+ * caller; the library never allocates, frees, or synchronises (the
+ * general-stride calls below take a caller-provided workspace instead). The caller
  * allocates C (as on the pages, where the host allocates the output and the
  * kernel writes into it). Work is enqueued on `stream` (a hipStream_t; NULL
  * means the null stream) and the call returns right after the enqueue, so a
@@ -43,6 +44,7 @@
 #ifndef MMRELU_H
 #define MMRELU_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -103,6 +105,52 @@ const char *mmrelu_status_string(int status);
 
 /* Library version string. */
 const char *mmrelu_version(void);
+
+/*
+ * General strides (widening of the interface above). The lecture describes a
+ * stored matrix by two strides, the position of element (row, column) being
+ * row * row_stride + column * column_stride, and a transpose as the same data
+ * with the two strides exchanged ("Kernels, Triton, XLA", section "Reductions
+ * and tiling"); the Chinese notes' section 5.5 kernel takes a stride for each
+ * dimension of A, B and C. Here, in ELEMENTS:
+ *     A[i][k] = A[i*sam + k*sak],  B[k][j] = B[k*sbk + j*sbn],  C[i][j] = C[i*scm + j*scn]
+ * and C[i][j] = act(sum_{k<K} A[i][k] * B[k][j] + bias[j]) as for the fused
+ * entry points (same act codes, bias of N elements or NULL).
+ *   - sam, sak, sbk, sbn >= 0 (a zero stride repeats an element); scm, scn >= 1
+ *     and the outputs must not overlap: scm >= N * scn or scn >= M * scm
+ *     (when M > 1 and N > 1). Every largest offset must stay below 2^60.
+ *   - Row-major operands and output (unit column stride, row stride within
+ *     the leading-dimension limits) are used in place, as by mmrelu_fused_*.
+ *     A column-major C (scm = 1) with no bias is computed as C^T = B^T A^T with
+ *     the operands' roles exchanged, also in place; so are transposed operands
+ *     that this exchange turns row-major (sam = 1 and sbk = 1 into scm = 1).
+ *   - Any other operand is first copied into row-major form, and any other C
+ *     is written from a row-major product, by a strided copy kernel through
+ *     the caller's WORKSPACE (device memory, 256-byte aligned, caller-owned,
+ *     not read before it is written; the library still allocates nothing).
+ *     An operand whose leading dimension or address would keep a 16-byte-
+ *     vector kernel out is also copied when the shape itself allows one.
+ *   - mmrelu_strided_workspace_size writes the bytes a call with the same
+ *     arguments needs (0 when everything is used in place). Pass the same
+ *     pointers: their alignment is part of the decision.
+ * Work (copies, product, copy-out) is enqueued in order on `stream`; the
+ * workspace must stay allocated until it completes, and calls sharing one
+ * workspace must be ordered (e.g. on one stream).
+ * Errors: as for the fused entry points, checked before anything is
+ * enqueued, plus MMRELU_ERR_INVALID_VALUE for a stride outside the rules above
+ * or workspace_bytes below the size needed, MMRELU_ERR_NULL_POINTER for a
+ * null workspace when one is needed, MMRELU_ERR_MISALIGNED for a workspace
+ * not 256-byte aligned.
+ */
+int mmrelu_strided_workspace_size(int dtype, int act, const void *A, const void *B, const void *bias, const void *C,
+                                  int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk,
+                                  int64_t sbn, int64_t scm, int64_t scn, size_t *bytes);
+int mmrelu_strided_f32(int act, const float *A, const float *B, const float *bias, float *C,
+                       int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
+                       int64_t scm, int64_t scn, void *workspace, size_t workspace_bytes, void *stream);
+int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, uint16_t *C,
+                        int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
+                        int64_t scm, int64_t scn, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Host-only planning (no GPU needed): which kernel variant and grid a call

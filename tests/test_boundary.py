@@ -224,3 +224,88 @@ def test_python_wrapper_rejects_bad_tensors():
         mm.mmrelu(torch.zeros(2, 2), torch.zeros(2, 2, dtype=torch.float64))
     with pytest.raises(ValueError):
         mm.mmrelu(torch.zeros(2, 2), torch.zeros(2, 2))   # host tensors
+
+
+# --- general strides: host-side planning and validation (no launch) ---------
+
+_P = 1 << 20          # 16-byte aligned stand-in addresses; nothing is launched
+
+
+def _ws(dt, M, N, K, sam, sak, sbk, sbn, scm, scn, bias=0, act=mm.ACT_RELU, a=_P, b=2 * _P, c=3 * _P):
+    return mm.mmrelu_strided_workspace_size(dt, act, a, b, bias, c, M, N, K, sam, sak, sbk, sbn, scm, scn)
+
+
+def _rup(x, q):
+    return (x + q - 1) // q * q
+
+
+def test_strided_workspace_plans():
+    M, N, K = 512, 256, 128
+    for dt, es in ((mm.DTYPE_F32, 4), (mm.DTYPE_BF16, 2)):
+        assert _ws(dt, M, N, K, K, 1, N, 1, N, 1) == 0                       # row-major: in place
+        assert _ws(dt, M, N, K, K + 64, 1, N + 32, 1, N + 16, 1) == 0        # padded rows: in place
+        assert _ws(dt, M, N, K, 1, M, N, 1, N, 1) == M * K * es              # A^T: A packed
+        assert _ws(dt, M, N, K, K, 1, 1, K, N, 1) == K * N * es              # B^T: B packed
+        assert _ws(dt, M, N, K, 1, M, 1, K, N, 1) == (M * K + K * N) * es    # both
+        assert _ws(dt, M, N, K, 1, M, 1, K, 1, M) == 0                       # TT into column-major C: swap
+        # NN into column-major C: swap packs both operands (K*(M+N)) < temporary C (M*N)
+        assert _ws(dt, M, N, K, K, 1, N, 1, 1, M) == (M * K + K * N) * es
+        # a bias rules the swap out: row-major temporary C
+        assert _ws(dt, M, N, K, 1, M, 1, K, 1, M, bias=4 * _P) == (M * K + K * N + M * N) * es
+        # long K: the temporary C is smaller than packing both operands
+        assert _ws(dt, 128, 128, 4096, 4096, 1, 128, 1, 1, 128) == 128 * 128 * es
+        # sub-sampled views are packed
+        assert _ws(dt, M, N, K, 6 * K, 3, 2 * N, 2, N, 1) == (M * K + K * N) * es
+        # empty outputs need nothing
+        assert _ws(dt, 0, N, K, 1, 1, 1, 1, 1, 1) == 0
+    # bf16 shape that allows 16-byte vectors: a row-major A with an odd ld is packed
+    assert _ws(mm.DTYPE_BF16, M, N, K, K + 1, 1, N, 1, N, 1) == M * K * 2
+    # ... a misaligned pointer too, and the packed ld is rounded up to 8 elements
+    assert _ws(mm.DTYPE_BF16, M, N, 120, 120, 1, N, 1, N, 1, a=_P + 2) == M * 120 * 2
+    # a shape that rules the vector kernels out anyway keeps row-major operands in place
+    assert _ws(mm.DTYPE_BF16, M, 100, K, K + 1, 1, 100, 1, 100, 1) == 0
+    # packed operands get 256-byte aligned slots
+    assert _ws(mm.DTYPE_F32, 3, 4, 5, 1, 3, 1, 5, 4, 1) == _rup(3 * 8 * 4, 256) + _rup(5 * 4 * 4, 256)
+
+
+def test_strided_validation():
+    M, N, K = 64, 32, 16
+    bad = [
+        (M, N, K, -1, 1, N, 1, N, 1),        # negative stride
+        (M, N, K, K, 1, N, 1, N, 0),         # zero output stride
+        (M, N, K, K, 1, N, 1, 1, 1),         # outputs overlap
+        (M, N, K, K, 1, N, 1, N - 1, 1),     # rows of C overlap
+        (M, N, K, 1 << 59, 1 << 59, N, 1, N, 1),    # offset past 2^60
+        (-1, N, K, K, 1, N, 1, N, 1),
+    ]
+    for args in bad:
+        with pytest.raises(mm.MmreluError) as e:
+            _ws(mm.DTYPE_F32, *args)
+        assert e.value.status == mm.MMRELU_ERR_INVALID_VALUE, args
+    with pytest.raises(mm.MmreluError) as e:
+        _ws(mm.DTYPE_F32, M, N, K, K, 1, N, 1, N, 1, act=7)
+    assert e.value.status == mm.MMRELU_ERR_INVALID_VALUE
+    with pytest.raises(mm.MmreluError) as e:
+        _ws(mm.DTYPE_F32, M, N, K, K, 1, N, 1, N, 1, a=_P + 2)
+    assert e.value.status == mm.MMRELU_ERR_MISALIGNED
+    with pytest.raises(mm.MmreluError) as e:
+        _ws(mm.DTYPE_F32, M, N, K, K, 1, N, 1, N, 1, c=0)
+    assert e.value.status == mm.MMRELU_ERR_NULL_POINTER
+    # zero strides in A and B (repeated elements) are allowed
+    assert _ws(mm.DTYPE_F32, M, N, K, 0, 1, N, 0, N, 1) >= 0
+
+
+def test_strided_entry_points_check_workspace_before_launch():
+    M, N, K = 64, 32, 16
+    need = _ws(mm.DTYPE_F32, M, N, K, 1, M, N, 1, N, 1)
+    assert need == M * K * 4
+    args = (mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, M, N, K, 1, M, N, 1, N, 1)
+    assert mm.mmrelu_strided_f32(*args, 0, need) == mm.MMRELU_ERR_NULL_POINTER
+    assert mm.mmrelu_strided_f32(*args, 4 * _P, need - 1) == mm.MMRELU_ERR_INVALID_VALUE
+    assert mm.mmrelu_strided_f32(*args, 4 * _P + 16, need) == mm.MMRELU_ERR_MISALIGNED
+    assert mm.mmrelu_strided_bf16(*args, 0, need) == mm.MMRELU_ERR_NULL_POINTER
+    # invalid strides come back before the workspace is looked at
+    assert mm.mmrelu_strided_f32(mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, M, N, K, 1, M, N, 1, 1, 1, 0, 0) == \
+        mm.MMRELU_ERR_INVALID_VALUE
+    # empty outputs: nothing to do, no workspace
+    assert mm.mmrelu_strided_f32(mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 0, N, K, 1, 1, 1, 1, 1, 1, 0, 0) == mm.MMRELU_OK

@@ -37,6 +37,7 @@ EXPORTED = (
     "mmrelu_plan", "mmrelu_num_variants", "mmrelu_plan_variant",
     "mmrelu_wave_quantization", "mmrelu_f32_variant", "mmrelu_bf16_variant",
     "mmrelu_fused_f32", "mmrelu_fused_bf16", "mmrelu_fused_f32_variant", "mmrelu_fused_bf16_variant",
+    "mmrelu_strided_workspace_size", "mmrelu_strided_f32", "mmrelu_strided_bf16",
 )
 
 
@@ -90,6 +91,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [i32, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
         fn.restype = ctypes.c_int
+    for name in ("mmrelu_strided_f32", "mmrelu_strided_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, vp,
+                       ctypes.c_size_t, vp]
+        fn.restype = ctypes.c_int
+    lib.mmrelu_strided_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                  i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mmrelu_strided_workspace_size.restype = ctypes.c_int
     lib.mmrelu_status_string.argtypes = [ctypes.c_int]
     lib.mmrelu_status_string.restype = ctypes.c_char_p
     lib.mmrelu_version.restype = ctypes.c_char_p
@@ -167,6 +176,32 @@ def mmrelu_fused_bf16_variant(variant: int, act: int, A: int, B: int, bias: int,
                                                     stream)
 
 
+def mmrelu_strided_workspace_size(dtype: int, act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int,
+                                  sam: int, sak: int, sbk: int, sbn: int, scm: int, scn: int) -> int:
+    """Workspace bytes a general-stride call with these arguments needs (raises on invalid arguments)."""
+    n = ctypes.c_size_t()
+    _check(load_library().mmrelu_strided_workspace_size(dtype, act, A or None, B or None, bias or None, C or None,
+                                                        M, N, K, sam, sak, sbk, sbn, scm, scn, ctypes.byref(n)),
+           "mmrelu_strided_workspace_size")
+    return n.value
+
+
+def mmrelu_strided_f32(act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int, sam: int, sak: int,
+                       sbk: int, sbn: int, scm: int, scn: int, workspace: int, workspace_bytes: int,
+                       stream: int = 0) -> int:
+    """Enqueue C = act(A·B + bias), fp32, with an element stride per dimension of A, B and C."""
+    return load_library().mmrelu_strided_f32(act, A, B, bias or None, C, M, N, K, sam, sak, sbk, sbn, scm, scn,
+                                             workspace or None, workspace_bytes, stream)
+
+
+def mmrelu_strided_bf16(act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int, sam: int, sak: int,
+                        sbk: int, sbn: int, scm: int, scn: int, workspace: int, workspace_bytes: int,
+                        stream: int = 0) -> int:
+    """Enqueue C = act(A·B + bias), bf16 in/out, with an element stride per dimension of A, B and C."""
+    return load_library().mmrelu_strided_bf16(act, A, B, bias or None, C, M, N, K, sam, sak, sbk, sbn, scm, scn,
+                                              workspace or None, workspace_bytes, stream)
+
+
 def mmrelu_plan(dtype: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, cus: int = 0) -> dict:
     p = Plan()
     _check(load_library().mmrelu_plan(dtype, M, N, K, lda, ldb, ldc, cus, ctypes.byref(p)), "mmrelu_plan")
@@ -200,15 +235,21 @@ def _ld(t) -> int:
     return max(t.stride(0), t.shape[1], 1)
 
 
+def _row_major(t) -> bool:
+    return t.dim() == 2 and (t.stride(1) == 1 or t.shape[1] <= 1) and t.stride(0) >= max(t.shape[1], 1)
+
+
 def mmrelu(a, b, out=None, variant: int | None = None, stream=None, bias=None, act: str = "relu"):
-    """act(a @ b + bias) for torch device tensors (float32 or bfloat16,
-    row-major); the default is relu(a @ b).
+    """act(a @ b + bias) for torch device tensors (float32 or bfloat16); the
+    default is relu(a @ b).
 
     ``bias`` is an optional contiguous (N,) tensor of the same dtype and
     ``act`` one of "relu", "gelu_tanh", "none". ``out`` may be a preallocated
-    (M, N) tensor (possibly a row-strided view). Launches on ``stream``
-    (default: torch's current stream) and returns ``out`` without
-    synchronising."""
+    (M, N) tensor. Row-major operands (unit column stride) go to the
+    row-major entry points; any other strides (transposed or sliced views)
+    go to the general-stride entry points with a workspace allocated here.
+    Launches on ``stream`` (default: torch's current stream) and returns
+    ``out`` without synchronising."""
     import torch
     if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("a and b must both be float32 or both bfloat16")
@@ -228,6 +269,23 @@ def mmrelu(a, b, out=None, variant: int | None = None, stream=None, bias=None, a
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous (N,) tensor of the inputs' dtype and device")
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    if not (_row_major(a) and _row_major(b) and _row_major(out)):
+        if variant is not None:
+            raise ValueError("an explicit variant needs row-major a, b and out")
+        kind = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_BF16
+        bp = bias.data_ptr() if bias is not None else 0
+        strides = (a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1))
+        need = mmrelu_strided_workspace_size(kind, _ACTS[act], a.data_ptr(), b.data_ptr(), bp, out.data_ptr(),
+                                             M, N, K, *strides)
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=a.device) if need else None
+        wp = 0
+        if ws is not None:
+            wp = (ws.data_ptr() + 255) // 256 * 256
+            ws.record_stream(s)
+        fn = mmrelu_strided_f32 if kind == DTYPE_F32 else mmrelu_strided_bf16
+        _check(fn(_ACTS[act], a.data_ptr(), b.data_ptr(), bp, out.data_ptr(), M, N, K, *strides, wp, need,
+                  s.cuda_stream), "mmrelu (strided)")
+        return out
     args = (a.data_ptr(), b.data_ptr(), bias.data_ptr() if bias is not None else 0, out.data_ptr(), M, N, K,
             _ld(a), _ld(b), _ld(out), s.cuda_stream)
     if a.dtype == torch.float32:

@@ -48,7 +48,6 @@ namespace mmrelu {
 namespace {
 
 constexpr int kWaves = 8, kThreads = kWaves * 64;
-constexpr int kWaveLdsBytes = 20 * 1024;          // per-wave ring budget (8 waves: 160 KB)
 
 template <typename T>
 struct KBlock;

@@ -54,4 +54,10 @@ const Variant *variant_bf16_mfma128();
 const Variant *variant_f32_skinny(int mb, int nb, int ks);
 const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 
+// Strided 2-D copy (k_pack.hip): dst[r][c] = src[r][c] for r < rows, c < cols,
+// element strides (s_r, s_c) and (d_r, d_c); esize 4 or 2. Enqueues nothing
+// for an empty copy.
+hipError_t launch_pack(int esize, const void *src, void *dst, int64_t rows, int64_t cols, int64_t s_r,
+                       int64_t s_c, int64_t d_r, int64_t d_c, hipStream_t stream);
+
 }  // namespace mmrelu

@@ -195,6 +195,160 @@ int run(int dtype, int32_t variant, int act, const void *A, const void *B, const
     return e == hipSuccess ? MMRELU_OK : MMRELU_ERR_LAUNCH;
 }
 
+// General strides: A[i][k] = A[i*sam + k*sak], B[k][j] = B[k*sbk + j*sbn],
+// C[i][j] = C[i*scm + j*scn]. The product that runs is row-major; operands
+// and outputs not already in that layout go through the caller's workspace.
+struct StridedPlan {
+    bool swap = false;                // run C^T = B^T·A^T (C column-major, no bias)
+    int64_t M = 0, N = 0, K = 0;      // of the row-major product that runs
+    const void *x = nullptr;          // its left operand in the caller's memory, strides (xr, xc)
+    const void *y = nullptr;          // its right operand, strides (yr, yc)
+    int64_t xr = 0, xc = 0, yr = 0, yc = 0;
+    bool pack_x = false, pack_y = false, temp_out = false;
+    int64_t ldx = 1, ldy = 1, ldz = 1;
+    size_t off_x = 0, off_y = 0, off_z = 0, bytes = 0;
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t &out) { return !__builtin_mul_overflow(a, b, &out); }
+
+// Largest element offset (rows-1)*s_r + (cols-1)*s_c, or -1 on overflow.
+int64_t extent(int64_t rows, int64_t cols, int64_t s_r, int64_t s_c)
+{
+    int64_t a = 0, b = 0, sum = 0;
+    if (rows <= 0 || cols <= 0) return 0;
+    if (!mul_ok(rows - 1, s_r, a) || !mul_ok(cols - 1, s_c, b) || __builtin_add_overflow(a, b, &sum)) return -1;
+    return sum < (int64_t{1} << 60) ? sum : -1;
+}
+
+size_t round_up(size_t x, size_t q) { return (x + q - 1) / q * q; }
+
+int plan_strided(int dtype, int act, const void *A, const void *B, const void *bias, const void *C, int64_t M,
+                 int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
+                 StridedPlan &p)
+{
+    if (dtype != MMRELU_DTYPE_F32 && dtype != MMRELU_DTYPE_BF16) return MMRELU_ERR_INVALID_VALUE;
+    if (act != MMRELU_ACT_RELU && act != MMRELU_ACT_GELU_TANH && act != MMRELU_ACT_NONE) return MMRELU_ERR_INVALID_VALUE;
+    const int64_t esize = dtype == MMRELU_DTYPE_F32 ? 4 : 2, q = 16 / esize;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return MMRELU_ERR_INVALID_VALUE;
+    if (sam < 0 || sak < 0 || sbk < 0 || sbn < 0 || scm < 1 || scn < 1) return MMRELU_ERR_INVALID_VALUE;
+    if (extent(M, K, sam, sak) < 0 || extent(K, N, sbk, sbn) < 0 || extent(M, N, scm, scn) < 0)
+        return MMRELU_ERR_INVALID_VALUE;
+    // Distinct outputs at distinct addresses: rows (or columns) of C occupy
+    // disjoint ranges.
+    if (M > 1 && N > 1) {
+        int64_t span_row = 0, span_col = 0;
+        const bool rows_apart = mul_ok(scn, N, span_row) && scm >= span_row;
+        const bool cols_apart = mul_ok(scm, M, span_col) && scn >= span_col;
+        if (!rows_apart && !cols_apart) return MMRELU_ERR_INVALID_VALUE;
+    }
+    int rc = check_pointers(A, B, C, M, N, K, static_cast<size_t>(esize));
+    if (rc != MMRELU_OK) return rc;
+    if (bias != nullptr && reinterpret_cast<uintptr_t>(bias) % esize != 0) return MMRELU_ERR_MISALIGNED;
+
+    p = StridedPlan{};
+    if (M == 0 || N == 0) return MMRELU_OK;
+    auto al16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    // A matrix is taken as it is when it is row-major with a leading dimension
+    // the kernels accept; when the product's K and N allow the 16-byte-vector
+    // kernels, also only if it does not keep them out (ld and pointer aligned).
+    auto usable = [&](const void *ptr, int64_t r, int64_t c, int64_t cols, bool dims_aligned) {
+        if (c != 1 || r < std::max<int64_t>(1, cols) || r > kMaxLd) return false;
+        return !dims_aligned || (r % q == 0 && al16(ptr));
+    };
+    const bool aligned_mn = K % q == 0 && N % q == 0, aligned_nm = K % q == 0 && M % q == 0;
+    // One way of running the call (swap or not, C in place or through a
+    // row-major temporary of leading dimension ldz) and its workspace layout.
+    auto build = [&](bool swap, bool temp_out, int64_t ldz) {
+        StridedPlan c;
+        c.swap = swap;
+        c.temp_out = temp_out;
+        c.ldz = ldz;
+        if (swap) {
+            c.M = N; c.N = M; c.K = K;
+            c.x = B; c.xr = sbn; c.xc = sbk;            // B^T[j][k] = B[k][j]
+            c.y = A; c.yr = sak; c.yc = sam;            // A^T[k][i] = A[i][k]
+        } else {
+            c.M = M; c.N = N; c.K = K;
+            c.x = A; c.xr = sam; c.xc = sak;
+            c.y = B; c.yr = sbk; c.yc = sbn;
+        }
+        const bool dims_aligned = c.K % q == 0 && c.N % q == 0;
+        if (c.K > 0) {
+            if (usable(c.x, c.xr, c.xc, c.K, dims_aligned)) {
+                c.ldx = c.xr;
+            } else {
+                c.pack_x = true;
+                c.ldx = static_cast<int64_t>(round_up(static_cast<size_t>(c.K), static_cast<size_t>(q)));
+            }
+            if (usable(c.y, c.yr, c.yc, c.N, dims_aligned)) {
+                c.ldy = c.yr;
+            } else {
+                c.pack_y = true;
+                c.ldy = static_cast<int64_t>(round_up(static_cast<size_t>(c.N), static_cast<size_t>(q)));
+            }
+        } else {
+            c.ldx = 1;
+            c.ldy = std::max<int64_t>(1, c.N);
+        }
+        size_t off = 0;
+        auto take = [&](bool used, int64_t rows, int64_t ld, size_t &at) {
+            if (!used) return;
+            at = off;
+            off += round_up(static_cast<size_t>(rows) * static_cast<size_t>(ld) * static_cast<size_t>(esize), 256);
+        };
+        take(c.pack_x, c.M, c.ldx, c.off_x);
+        take(c.pack_y, c.K, c.ldy, c.off_y);
+        take(c.temp_out, c.M, c.ldz, c.off_z);
+        c.bytes = off;
+        return c;
+    };
+    const int64_t ld_temp = static_cast<int64_t>(round_up(static_cast<size_t>(N), static_cast<size_t>(q)));
+    if (usable(C, scm, scn, N, aligned_mn)) {
+        p = build(false, false, scm);
+    } else {
+        // C not row-major: through a row-major temporary, or (no bias, C
+        // column-major) as C^T = B^T·A^T in place; the route that copies
+        // fewer bytes through the workspace.
+        p = build(false, true, ld_temp);
+        if (bias == nullptr && usable(C, scn, scm, M, aligned_nm)) {
+            const StridedPlan sw = build(true, false, scn);
+            if (sw.bytes <= p.bytes) p = sw;
+        }
+    }
+    if (p.ldx > kMaxLd || p.ldy > kMaxLd || p.ldz > kMaxLd) return MMRELU_ERR_INVALID_VALUE;
+    return check_shape(p.M, p.N, p.K, p.ldx, p.ldy, p.ldz);
+}
+
+int run_strided(int dtype, int act, const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
+                int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
+                void *workspace, size_t workspace_bytes, void *stream)
+{
+    StridedPlan p;
+    int rc = plan_strided(dtype, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, p);
+    if (rc != MMRELU_OK) return rc;
+    if (M == 0 || N == 0) return MMRELU_OK;
+    if (p.bytes > 0) {
+        if (workspace == nullptr) return MMRELU_ERR_NULL_POINTER;
+        if (workspace_bytes < p.bytes) return MMRELU_ERR_INVALID_VALUE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return MMRELU_ERR_MISALIGNED;
+    }
+    const int esize = dtype == MMRELU_DTYPE_F32 ? 4 : 2;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const void *x = p.pack_x ? ws + p.off_x : p.x;
+    const void *y = p.pack_y ? ws + p.off_y : p.y;
+    void *z = p.temp_out ? ws + p.off_z : C;
+    if (p.pack_x && launch_pack(esize, p.x, ws + p.off_x, p.M, p.K, p.xr, p.xc, p.ldx, 1, s) != hipSuccess)
+        return MMRELU_ERR_LAUNCH;
+    if (p.pack_y && launch_pack(esize, p.y, ws + p.off_y, p.K, p.N, p.yr, p.yc, p.ldy, 1, s) != hipSuccess)
+        return MMRELU_ERR_LAUNCH;
+    rc = run(dtype, -1, act, x, y, bias, z, p.M, p.N, p.K, p.ldx, p.ldy, p.ldz, stream);
+    if (rc != MMRELU_OK) return rc;
+    if (p.temp_out && launch_pack(esize, ws + p.off_z, C, M, N, p.ldz, 1, scm, scn, s) != hipSuccess)
+        return MMRELU_ERR_LAUNCH;
+    return MMRELU_OK;
+}
+
 }  // namespace
 }  // namespace mmrelu
 
@@ -253,6 +407,33 @@ int mmrelu_fused_bf16_variant(int32_t variant, int act, const uint16_t *A, const
 {
     if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
     return run(MMRELU_DTYPE_BF16, variant, act, A, B, bias, C, M, N, K, lda, ldb, ldc, stream);
+}
+
+int mmrelu_strided_workspace_size(int dtype, int act, const void *A, const void *B, const void *bias, const void *C,
+                                  int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk,
+                                  int64_t sbn, int64_t scm, int64_t scn, size_t *bytes)
+{
+    if (bytes == nullptr) return MMRELU_ERR_NULL_POINTER;
+    StridedPlan p;
+    const int rc = plan_strided(dtype, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, p);
+    *bytes = rc == MMRELU_OK ? p.bytes : 0;
+    return rc;
+}
+
+int mmrelu_strided_f32(int act, const float *A, const float *B, const float *bias, float *C, int64_t M, int64_t N,
+                       int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm, int64_t scn,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_strided(MMRELU_DTYPE_F32, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, workspace,
+                       workspace_bytes, stream);
+}
+
+int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, uint16_t *C, int64_t M,
+                        int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm,
+                        int64_t scn, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_strided(MMRELU_DTYPE_BF16, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, workspace,
+                       workspace_bytes, stream);
 }
 
 const char *mmrelu_status_string(int status)
