@@ -247,6 +247,66 @@ def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="re
             "b2b_ms": round(b2b, 5), "alg_gbs_b2b": round(alg_bytes / (b2b * 1e-3) / 1e9, 1)}
 
 
+LAYOUTS = {   # name: (A stored as, B stored as, C stored as); "col" = the transpose's row-major storage
+    "NN": ("row", "row", "row"), "TN": ("col", "row", "row"), "NT": ("row", "col", "row"),
+    "TT": ("col", "col", "row"), "TT_Ccol": ("col", "col", "col"), "NN_Ccol": ("row", "row", "col"),
+}
+
+
+def layout_stats(cfg, name, steps, warmup, torch, mm, datagen):
+    """Per-call and back-to-back times of one workload with its operands and
+    output stored in the layout `name` (general-stride entry points, the
+    workspace allocated once outside the timed calls)."""
+    import numpy as np
+    a, b = datagen.make_inputs(cfg)
+    la, lb, lc = LAYOUTS[name]
+    M, N, K = cfg.M, cfg.N, cfg.K
+    a = a[:, :K] if cfg.lda != K else a
+    b = b[:, :N] if cfg.ldb != N else b
+    if la == "col":
+        da, sa = to_device(np.ascontiguousarray(a.T), torch), (1, M)
+    else:
+        da, sa = to_device(np.ascontiguousarray(a), torch), (K, 1)
+    if lb == "col":
+        db, sb = to_device(np.ascontiguousarray(b.T), torch), (1, K)
+    else:
+        db, sb = to_device(np.ascontiguousarray(b), torch), (N, 1)
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    c = torch.empty((N, M) if lc == "col" else (M, N), dtype=dt, device="cuda")
+    sc = (1, M) if lc == "col" else (N, 1)
+    kind = mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16
+    need = mm.mmrelu_strided_workspace_size(kind, mm.ACT_RELU, da.data_ptr(), db.data_ptr(), 0, c.data_ptr(),
+                                            M, N, K, *sa, *sb, *sc)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    fn = mm.mmrelu_strided_f32 if kind == mm.DTYPE_F32 else mm.mmrelu_strided_bf16
+    stream = torch.cuda.current_stream()
+    args = (mm.ACT_RELU, da.data_ptr(), db.data_ptr(), 0, c.data_ptr(), M, N, K, *sa, *sb, *sc,
+            ws.data_ptr() if need else 0, need, stream.cuda_stream)
+    for _ in range(warmup):
+        rc = fn(*args)
+        if rc != mm.MMRELU_OK:
+            raise RuntimeError(mm.status_string(rc))
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(*args)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b = e0.elapsed_time(e1) / steps
+    med = t[steps // 2]
+    return {"workload": cfg.name, "layout": name, "A": la, "B": lb, "C": lc, "workspace_bytes": need,
+            "median_ms": round(med, 5), "b2b_ms": round(b2b, 5),
+            "tflops_b2b": round(cfg.flops / (b2b * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(cfg, a, b, target_s, oracle):
     """The oracle timed on rows [0, r) of the workload, r chosen from a short
     calibration run so that the timed part takes about target_s seconds."""
@@ -290,6 +350,10 @@ def main():
                     help="instead of the benchmark line: square sizes 256..8192 and skinny shapes (M or N of "
                          "1..64, the others 8192) in both dtypes, per-call statistics with the bounding roofline "
                          "(MFMA or HBM) and the fraction of it reached, one JSON line each")
+    ap.add_argument("--layouts", action="store_true",
+                    help="instead of the benchmark line: the bf16 8192^3 and fp32 4096^3 workloads with A, B and C "
+                         "stored row- or column-major (NN, TN, NT, TT, TT into a column-major C, NN into a "
+                         "column-major C) through the general-stride entry points, one JSON line each")
     ap.add_argument("--shapes", default="",
                     help="with --sweep: only these shapes, comma-separated dtype:MxNxK (e.g. f32:1x8192x8192)")
     ap.add_argument("--sweep-steps", type=int, default=0,
@@ -349,6 +413,24 @@ def main():
             r["pct_of_hbm_peak"] = round(100 * r["alg_gbs_median"] / HBM_PEAK_GBS, 2)
             r["roofline_frac_b2b"] = round(max(t_mfma, t_hbm) / r["b2b_ms"], 4)
             print(json.dumps(r), flush=True)
+        return
+
+    if args.layouts:
+        import torch
+        import datagen
+        import tiled_matmul_relu_amd as mm
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        mm.load_library()
+        for cid in (5, 3):
+            cfg = datagen.CONFIGS[cid]
+            base = None
+            for name in LAYOUTS:
+                r = layout_stats(cfg, name, args.sweep_steps or 40, 10, torch, mm, datagen)
+                base = base or r["b2b_ms"]
+                r["vs_NN"] = round(r["b2b_ms"] / base, 4)
+                print(json.dumps(r), flush=True)
         return
 
     if args.counter_summary:
