@@ -9,8 +9,9 @@ built with gcc into ``liboracle.so`` next to it. Each routine is the plain
 definition R[i][j] = max(0, sum_k A[i][k]·B[k][j]) in fp64 with ascending k,
 its fused-epilogue form R[i][j] = act(sum_k A[i][k]·B[k][j] + bias[j])
 with act one of ReLU, GeLU (tanh form) or none, and its general-stride form
-(A[i][k] = a[i*sam + k*sak], B[k][j] = b[k*sbk + j*sbn]); see the C file for
-the passages it follows.
+(A[i][k] = a[i*sam + k*sak], B[k][j] = b[k*sbk + j*sbn]). It also holds the
+two rungs before the matmul on the lecture's ladder: the row softmax and the
+row sum. See the C file for the passages each follows.
 """
 from __future__ import annotations
 
@@ -67,6 +68,14 @@ def _load():
     for name in ("oracle_strided_f32_at", "oracle_strided_bf16_at"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_int, p, p, p, i64, i64, i64, i64, i64, p, p, i64, p]
+        fn.restype = None
+    for name in ("oracle_softmax_rows_f32", "oracle_softmax_rows_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, i64, i64, i64]
+        fn.restype = ctypes.c_int
+    for name in ("oracle_row_sum_f32", "oracle_row_sum_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, i64, i64, i64]
         fn.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -245,3 +254,42 @@ def strided_at(act: str, a: np.ndarray, b: np.ndarray, bias, rows, cols, M: int,
         getattr(_load(), fn)(ACTS[act], a.ctypes.data, b.ctypes.data, bp, K, sam, sak, sbk, sbn,
                              ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
     return out
+
+
+def _rows(x: np.ndarray, M, N, ldx):
+    dtype, _, _ = _dtype_and_fns(x)
+    if not x.flags.c_contiguous:
+        raise ValueError("oracle inputs must be C-contiguous buffers")
+    if M is None:
+        M, N = x.shape
+        ldx = max(N, 1)
+    ldx = ldx if ldx is not None else max(N, 1)
+    if min(M, N) < 0 or ldx < max(1, N):
+        raise ValueError("bad sizes or leading dimension")
+    if M > 0 and N > 0 and x.size < (M - 1) * ldx + N:
+        raise ValueError("X buffer too small")
+    return dtype, M, N, ldx
+
+
+def softmax_rows(x: np.ndarray, M=None, N=None, ldx=None) -> np.ndarray:
+    """Softmax of each row of X (M x N, leading dimension ldx) as an M x N
+    float64 array: exp(x - rowmax) / sum(exp(x - rowmax))."""
+    dtype, M, N, ldx = _rows(x, M, N, ldx)
+    r = np.empty((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return r
+    fn = "oracle_softmax_rows_f32" if dtype == np.float32 else "oracle_softmax_rows_bf16"
+    if getattr(_load(), fn)(x.ctypes.data, r.ctypes.data, M, N, ldx) != 0:
+        raise MemoryError("oracle could not allocate its row buffer")
+    return r
+
+
+def row_sum(x: np.ndarray, M=None, N=None, ldx=None) -> np.ndarray:
+    """Sum of each row of X (M x N, leading dimension ldx) as M float64 values."""
+    dtype, M, N, ldx = _rows(x, M, N, ldx)
+    r = np.zeros(M, dtype=np.float64)
+    if M == 0:
+        return r
+    fn = "oracle_row_sum_f32" if dtype == np.float32 else "oracle_row_sum_bf16"
+    getattr(_load(), fn)(x.ctypes.data, r.ctypes.data, M, N, ldx)
+    return r

@@ -246,3 +246,92 @@ void oracle_mmrelu_bf16_at(const uint16_t *A, const uint16_t *B, int64_t K,
 {
     oracle_fused_bf16_at(0, A, B, NULL, K, lda, ldb, ii, jj, n, out);
 }
+
+/*
+ * Row softmax and row sum (the rungs before the matmul on the lecture's
+ * ladder: "Kernels, Triton, XLA", section "Reductions and tiling", the
+ * softmax and row-sum paragraphs; the Chinese notes' sections 5.3 and 5.4).
+ * X is M x N, row-major with leading dimension ldx; inputs are finite
+ * (parity unpinned for infinities and NaN).
+ *
+ *   softmax: m = max_j X[i][j];  e_j = exp(X[i][j] - m);  s = sum_j e_j
+ *            (ascending j);  R[i][j] = e_j / s
+ *   row sum: R[i] = sum_j X[i][j] in ascending j
+ *
+ * all in double, with libm's exp; the result is row-major with ld N (softmax)
+ * or a vector of M (row sum). Subtracting the row maximum is what keeps exp
+ * finite for large inputs; mathematically it cancels in the quotient.
+ */
+static void softmax_row(const double *x, double *r, int64_t n)
+{
+    double m = x[0];
+    for (int64_t j = 1; j < n; ++j) m = x[j] > m ? x[j] : m;
+    double s = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        r[j] = exp(x[j] - m);
+        s += r[j];
+    }
+    for (int64_t j = 0; j < n; ++j) r[j] = r[j] / s;
+}
+
+int oracle_softmax_rows_f32(const float *X, double *R, int64_t M, int64_t N, int64_t ldx)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *x = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!x) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            if (!x || N == 0) continue;
+            for (int64_t j = 0; j < N; ++j) x[j] = (double)X[i * ldx + j];
+            softmax_row(x, R + i * N, N);
+        }
+        free(x);
+    }
+    return failed ? -1 : 0;
+}
+
+int oracle_softmax_rows_bf16(const uint16_t *X, double *R, int64_t M, int64_t N, int64_t ldx)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *x = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!x) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            if (!x || N == 0) continue;
+            for (int64_t j = 0; j < N; ++j) x[j] = widen_bf16(X[i * ldx + j]);
+            softmax_row(x, R + i * N, N);
+        }
+        free(x);
+    }
+    return failed ? -1 : 0;
+}
+
+void oracle_row_sum_f32(const float *X, double *R, int64_t M, int64_t N, int64_t ldx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j) s += (double)X[i * ldx + j];
+        R[i] = s;
+    }
+}
+
+void oracle_row_sum_bf16(const uint16_t *X, double *R, int64_t M, int64_t N, int64_t ldx)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j) s += widen_bf16(X[i * ldx + j]);
+        R[i] = s;
+    }
+}
