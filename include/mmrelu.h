@@ -153,6 +153,49 @@ int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uin
                         int64_t scm, int64_t scn, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Row softmax and row sum: the two rungs before the matmul on the lecture's
+ * ladder ("Kernels, Triton, XLA", section "Reductions and tiling", the softmax
+ * and row-sum paragraphs; the Chinese notes' sections 5.3 and 5.4). X is
+ * M x N, row-major with leading dimension ldx (elements), device memory.
+ *
+ *   softmax: Y[i][j] = exp(X[i][j] - m_i) / sum_j exp(X[i][j] - m_i),
+ *            m_i = max_j X[i][j]; computed in fp32 (bf16 inputs widened, bf16
+ *            outputs rounded once to nearest-even). Y is M x N with leading
+ *            dimension ldy >= N; Y may be X itself (in place, ldy == ldx),
+ *            otherwise the two must not overlap (not checked). Elements
+ *            beyond column N are neither read nor written.
+ *   row sum: out[i] = sum_j X[i][j], accumulated in fp32; out is M floats
+ *            for both input dtypes. N == 0 writes zeros.
+ *
+ * X must be finite (infinities and NaN are outside the contract). Work is
+ * enqueued on `stream`; arguments are checked first, and on any non-zero
+ * status nothing is launched. Errors: MMRELU_ERR_INVALID_VALUE for negative
+ * or too large sizes, ldx < max(1, N) (or ldy < max(1, N)), X == Y with
+ * ldx != ldy, or an offset past 2^60; MMRELU_ERR_NULL_POINTER for a null
+ * pointer that would be used; MMRELU_ERR_MISALIGNED for a pointer not aligned
+ * to its element size. Empty outputs (M == 0, or N == 0 for softmax) launch
+ * nothing.
+ *
+ * Softmax kernels (the _variant forms force one, for tests): 0, 1, 2 hold a
+ * row in registers and need N, ldx and ldy multiples of 16 / sizeof(element)
+ * with 16-byte aligned X and Y; they take rows of up to 1024, 4096 or 16384
+ * fp32 (2048, 8192 or 32768 bf16) columns. 3 reads each row twice with
+ * 16-byte vectors (same layout rule, any N); 4 reads single elements (any
+ * layout). mmrelu_softmax_rows_variant reports the choice for a shape,
+ * taking X and Y as 16-byte aligned.
+ */
+int mmrelu_softmax_rows_f32(const float *X, float *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy, void *stream);
+int mmrelu_softmax_rows_bf16(const uint16_t *X, uint16_t *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                             void *stream);
+int mmrelu_softmax_rows_f32_variant(int32_t variant, const float *X, float *Y, int64_t M, int64_t N, int64_t ldx,
+                                    int64_t ldy, void *stream);
+int mmrelu_softmax_rows_bf16_variant(int32_t variant, const uint16_t *X, uint16_t *Y, int64_t M, int64_t N,
+                                     int64_t ldx, int64_t ldy, void *stream);
+int mmrelu_softmax_rows_variant(int dtype, int64_t N, int64_t ldx, int64_t ldy, int32_t *variant);
+int mmrelu_row_sum_f32(const float *X, float *out, int64_t M, int64_t N, int64_t ldx, void *stream);
+int mmrelu_row_sum_bf16(const uint16_t *X, float *out, int64_t M, int64_t N, int64_t ldx, void *stream);
+
+/*
  * Host-only planning (no GPU needed): which kernel variant and grid a call
  * of this shape would use, and how its workgroups quantise into waves over
  * the compute units (the lecture's "wave quantization": a last, partial wave

@@ -309,3 +309,46 @@ def test_strided_entry_points_check_workspace_before_launch():
         mm.MMRELU_ERR_INVALID_VALUE
     # empty outputs: nothing to do, no workspace
     assert mm.mmrelu_strided_f32(mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 0, N, K, 1, 1, 1, 1, 1, 1, 0, 0) == mm.MMRELU_OK
+
+
+# --- row softmax and row sum: validation and kernel choice (no launch) -------
+
+def test_softmax_variant_choice():
+    F, B = mm.DTYPE_F32, mm.DTYPE_BF16
+    assert [mm.mmrelu_softmax_rows_variant(F, n, n, n) for n in (4, 1024, 1028, 4096, 4100, 16384, 16388)] == \
+        [0, 0, 1, 1, 2, 2, 3]
+    assert [mm.mmrelu_softmax_rows_variant(B, n, n, n) for n in (8, 2048, 2056, 8192, 8200, 32768, 32776)] == \
+        [0, 0, 1, 1, 2, 2, 3]
+    assert mm.mmrelu_softmax_rows_variant(F, 1001, 1001, 1001) == 4       # N not a multiple of 4
+    assert mm.mmrelu_softmax_rows_variant(F, 1000, 1001, 1000) == 4       # ldx not a multiple of 4
+    assert mm.mmrelu_softmax_rows_variant(B, 1004, 1004, 1004) == 4       # bf16 N not a multiple of 8
+    with pytest.raises(mm.MmreluError):
+        mm.mmrelu_softmax_rows_variant(F, 100, 99, 100)
+
+
+def test_row_ops_validate_before_launch():
+    s = mm.mmrelu_softmax_rows_f32
+    assert s(_P, 2 * _P, -1, 4, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    assert s(_P, 2 * _P, 4, 8, 4, 8) == mm.MMRELU_ERR_INVALID_VALUE        # ldx < N
+    assert s(_P, 2 * _P, 4, 8, 8, 4) == mm.MMRELU_ERR_INVALID_VALUE        # ldy < N
+    assert s(_P, _P, 4, 8, 8, 16) == mm.MMRELU_ERR_INVALID_VALUE           # in place with another ld
+    assert s(0, 2 * _P, 4, 8, 8, 8) == mm.MMRELU_ERR_NULL_POINTER
+    assert s(_P, 0, 4, 8, 8, 8) == mm.MMRELU_ERR_NULL_POINTER
+    assert s(_P + 2, 2 * _P, 4, 8, 8, 8) == mm.MMRELU_ERR_MISALIGNED
+    assert s(_P, 2 * _P, 4, 8, 1 << 59, 8) == mm.MMRELU_ERR_INVALID_VALUE  # offset past 2^60
+    assert s(_P, 2 * _P, 0, 8, 8, 8) == mm.MMRELU_OK                        # empty: nothing launched
+    assert s(_P, 2 * _P, 5, 0, 1, 1) == mm.MMRELU_OK
+    assert mm.mmrelu_softmax_rows_bf16(_P + 1, 2 * _P, 4, 8, 8, 8) == mm.MMRELU_ERR_MISALIGNED
+    v = mm.mmrelu_softmax_rows_f32_variant
+    assert v(9, _P, 2 * _P, 4, 8, 8, 8) == mm.MMRELU_ERR_INVALID_VALUE     # no such kernel
+    assert v(0, _P, 2 * _P, 4, 7, 7, 7) == mm.MMRELU_ERR_INVALID_VALUE     # vector kernel, N % 4 != 0
+    assert v(0, _P, 2 * _P, 4, 2048, 2048, 2048) == mm.MMRELU_ERR_INVALID_VALUE   # row too long for it
+    assert v(-1, _P, 2 * _P, 4, 8, 8, 8) == mm.MMRELU_ERR_INVALID_VALUE
+    r = mm.mmrelu_row_sum_f32
+    assert r(_P, 2 * _P, -1, 4, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    assert r(_P, 2 * _P, 4, 8, 4) == mm.MMRELU_ERR_INVALID_VALUE
+    assert r(_P, 0, 4, 8, 8) == mm.MMRELU_ERR_NULL_POINTER
+    assert r(0, 2 * _P, 4, 8, 8) == mm.MMRELU_ERR_NULL_POINTER
+    assert r(_P, 2 * _P + 2, 4, 8, 8) == mm.MMRELU_ERR_MISALIGNED          # out is fp32
+    assert mm.mmrelu_row_sum_bf16(_P + 1, 2 * _P, 4, 8, 8) == mm.MMRELU_ERR_MISALIGNED
+    assert r(_P, 2 * _P, 0, 8, 8) == mm.MMRELU_OK

@@ -38,6 +38,8 @@ EXPORTED = (
     "mmrelu_wave_quantization", "mmrelu_f32_variant", "mmrelu_bf16_variant",
     "mmrelu_fused_f32", "mmrelu_fused_bf16", "mmrelu_fused_f32_variant", "mmrelu_fused_bf16_variant",
     "mmrelu_strided_workspace_size", "mmrelu_strided_f32", "mmrelu_strided_bf16",
+    "mmrelu_softmax_rows_f32", "mmrelu_softmax_rows_bf16", "mmrelu_softmax_rows_f32_variant",
+    "mmrelu_softmax_rows_bf16_variant", "mmrelu_softmax_rows_variant", "mmrelu_row_sum_f32", "mmrelu_row_sum_bf16",
 )
 
 
@@ -99,6 +101,20 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mmrelu_strided_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64,
                                                   i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mmrelu_strided_workspace_size.restype = ctypes.c_int
+    for name in ("mmrelu_softmax_rows_f32", "mmrelu_softmax_rows_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    for name in ("mmrelu_softmax_rows_f32_variant", "mmrelu_softmax_rows_bf16_variant"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, vp, vp, i64, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
+    lib.mmrelu_softmax_rows_variant.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(i32)]
+    lib.mmrelu_softmax_rows_variant.restype = ctypes.c_int
+    for name in ("mmrelu_row_sum_f32", "mmrelu_row_sum_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, i64, i64, i64, vp]
+        fn.restype = ctypes.c_int
     lib.mmrelu_status_string.argtypes = [ctypes.c_int]
     lib.mmrelu_status_string.restype = ctypes.c_char_p
     lib.mmrelu_version.restype = ctypes.c_char_p
@@ -202,6 +218,44 @@ def mmrelu_strided_bf16(act: int, A: int, B: int, bias: int, C: int, M: int, N: 
                                               workspace or None, workspace_bytes, stream)
 
 
+def mmrelu_softmax_rows_f32(X: int, Y: int, M: int, N: int, ldx: int, ldy: int, stream: int = 0) -> int:
+    """Enqueue the row softmax of an fp32 M x N matrix; returns the status."""
+    return load_library().mmrelu_softmax_rows_f32(X or None, Y or None, M, N, ldx, ldy, stream)
+
+
+def mmrelu_softmax_rows_bf16(X: int, Y: int, M: int, N: int, ldx: int, ldy: int, stream: int = 0) -> int:
+    """Enqueue the row softmax of a bf16 M x N matrix (fp32 inside); returns the status."""
+    return load_library().mmrelu_softmax_rows_bf16(X or None, Y or None, M, N, ldx, ldy, stream)
+
+
+def mmrelu_softmax_rows_f32_variant(variant: int, X: int, Y: int, M: int, N: int, ldx: int, ldy: int,
+                                    stream: int = 0) -> int:
+    return load_library().mmrelu_softmax_rows_f32_variant(variant, X or None, Y or None, M, N, ldx, ldy, stream)
+
+
+def mmrelu_softmax_rows_bf16_variant(variant: int, X: int, Y: int, M: int, N: int, ldx: int, ldy: int,
+                                     stream: int = 0) -> int:
+    return load_library().mmrelu_softmax_rows_bf16_variant(variant, X or None, Y or None, M, N, ldx, ldy, stream)
+
+
+def mmrelu_softmax_rows_variant(dtype: int, N: int, ldx: int, ldy: int) -> int:
+    """The softmax kernel a call of this shape uses (16-byte aligned pointers)."""
+    v = ctypes.c_int32()
+    _check(load_library().mmrelu_softmax_rows_variant(dtype, N, ldx, ldy, ctypes.byref(v)),
+           "mmrelu_softmax_rows_variant")
+    return v.value
+
+
+def mmrelu_row_sum_f32(X: int, out: int, M: int, N: int, ldx: int, stream: int = 0) -> int:
+    """Enqueue out[i] = sum_j X[i][j] for an fp32 matrix (fp32 out); returns the status."""
+    return load_library().mmrelu_row_sum_f32(X or None, out or None, M, N, ldx, stream)
+
+
+def mmrelu_row_sum_bf16(X: int, out: int, M: int, N: int, ldx: int, stream: int = 0) -> int:
+    """Enqueue out[i] = sum_j X[i][j] for a bf16 matrix (fp32 out); returns the status."""
+    return load_library().mmrelu_row_sum_bf16(X or None, out or None, M, N, ldx, stream)
+
+
 def mmrelu_plan(dtype: int, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, cus: int = 0) -> dict:
     p = Plan()
     _check(load_library().mmrelu_plan(dtype, M, N, K, lda, ldb, ldc, cus, ctypes.byref(p)), "mmrelu_plan")
@@ -295,4 +349,37 @@ def mmrelu(a, b, out=None, variant: int | None = None, stream=None, bias=None, a
         rc = (mmrelu_fused_bf16(_ACTS[act], *args) if variant is None
               else mmrelu_fused_bf16_variant(variant, _ACTS[act], *args))
     _check(rc, "mmrelu")
+    return out
+
+
+def softmax_rows(x, out=None, stream=None):
+    """Row softmax of a 2-D float32 or bfloat16 device tensor (unit column
+    stride); ``out`` may be ``x`` itself. Returns ``out`` without
+    synchronising."""
+    import torch
+    if x.dim() != 2 or x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda:
+        raise ValueError("x must be a 2-D float32 or bfloat16 device tensor")
+    M, N = x.shape
+    out = torch.empty_like(x) if out is None else out
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    fn = mmrelu_softmax_rows_f32 if x.dtype == torch.float32 else mmrelu_softmax_rows_bf16
+    _check(fn(x.data_ptr(), out.data_ptr(), M, N, _ld(x), _ld(out), s.cuda_stream), "softmax_rows")
+    return out
+
+
+def row_sum(x, out=None, stream=None):
+    """Sum of each row of a 2-D float32 or bfloat16 device tensor (unit
+    column stride), as an (M,) float32 tensor. Returns without synchronising."""
+    import torch
+    if x.dim() != 2 or x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda:
+        raise ValueError("x must be a 2-D float32 or bfloat16 device tensor")
+    M, N = x.shape
+    out = torch.empty(M, dtype=torch.float32, device=x.device) if out is None else out
+    if out.shape != (M,) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (M,) float32 tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    fn = mmrelu_row_sum_f32 if x.dtype == torch.float32 else mmrelu_row_sum_bf16
+    _check(fn(x.data_ptr(), out.data_ptr(), M, N, _ld(x), s.cuda_stream), "row_sum")
     return out

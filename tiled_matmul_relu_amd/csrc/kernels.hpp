@@ -60,4 +60,15 @@ const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 hipError_t launch_pack(int esize, const void *src, void *dst, int64_t rows, int64_t cols, int64_t s_r,
                        int64_t s_c, int64_t d_r, int64_t d_c, hipStream_t stream);
 
+// Row softmax and row sum (k_rows.hip). Softmax variants 0-2 keep a row in
+// registers (up to softmax_capacity(variant, esize) columns; N % (16/esize)
+// == 0 and 16-byte aligned rows), 3 is two passes with 16-byte vectors (same
+// layout rule), 4 two passes over single elements (any layout).
+constexpr int kSoftmaxVariants = 5;
+int64_t softmax_capacity(int variant, int esize);
+hipError_t launch_softmax(int esize, int variant, const void *X, void *Y, int64_t M, int64_t N, int64_t ldx,
+                          int64_t ldy, hipStream_t stream);
+hipError_t launch_row_sum(int esize, bool vec, bool short_rows, const void *X, float *out, int64_t M, int64_t N,
+                          int64_t ldx, hipStream_t stream);
+
 }  // namespace mmrelu

@@ -349,6 +349,64 @@ int run_strided(int dtype, int act, const void *A, const void *B, const void *bi
     return MMRELU_OK;
 }
 
+// Row operations: shared argument checks. ld must cover the row and the
+// largest offset must stay below 2^60.
+int check_rows(const void *X, const void *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy, size_t esize_x,
+               size_t esize_y)
+{
+    if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return MMRELU_ERR_INVALID_VALUE;
+    if (ldx < std::max<int64_t>(1, N) || ldy < 1) return MMRELU_ERR_INVALID_VALUE;
+    if (extent(M, N, ldx, 1) < 0 || extent(M, 1, ldy, 1) < 0) return MMRELU_ERR_INVALID_VALUE;
+    if (M == 0) return MMRELU_OK;
+    if (X == nullptr && N > 0) return MMRELU_ERR_NULL_POINTER;
+    if (Y == nullptr) return MMRELU_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(X) % esize_x != 0 || reinterpret_cast<uintptr_t>(Y) % esize_y != 0)
+        return MMRELU_ERR_MISALIGNED;
+    return MMRELU_OK;
+}
+
+bool rows_vectorisable(const void *X, const void *Y, int64_t N, int64_t ldx, int64_t ldy, int64_t v)
+{
+    auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    return N % v == 0 && ldx % v == 0 && ldy % v == 0 && al16(X) && al16(Y);
+}
+
+int softmax_rows(int esize, int variant, const void *X, void *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                 void *stream)
+{
+    int rc = check_rows(X, Y, M, N, ldx, ldy, esize, esize);
+    if (rc != MMRELU_OK) return rc;
+    if (ldy < std::max<int64_t>(1, N) || extent(M, N, ldy, 1) < 0) return MMRELU_ERR_INVALID_VALUE;
+    if (X == Y && ldx != ldy) return MMRELU_ERR_INVALID_VALUE;       // in place: the same layout
+    const bool vec = rows_vectorisable(X, Y, N, ldx, ldy, 16 / esize);
+    if (variant < 0) {
+        variant = 4;
+        if (vec) {
+            variant = 3;
+            for (int v = 2; v >= 0; --v)
+                if (N <= softmax_capacity(v, esize)) variant = v;
+        }
+    } else if (variant >= kSoftmaxVariants || (variant < 4 && !vec) || N > softmax_capacity(variant, esize)) {
+        return MMRELU_ERR_INVALID_VALUE;
+    }
+    if (M == 0 || N == 0) return MMRELU_OK;
+    return launch_softmax(esize, variant, X, Y, M, N, ldx, ldy, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MMRELU_OK
+               : MMRELU_ERR_LAUNCH;
+}
+
+int row_sum_rows(int esize, const void *X, float *out, int64_t M, int64_t N, int64_t ldx, void *stream)
+{
+    int rc = check_rows(X, out, M, N, ldx, 1, esize, 4);
+    if (rc != MMRELU_OK) return rc;
+    if (M == 0) return MMRELU_OK;
+    const int64_t v = 16 / esize;
+    const bool vec = N % v == 0 && ldx % v == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+    return launch_row_sum(esize, vec, N <= 1024, X, out, M, N, ldx, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? MMRELU_OK
+               : MMRELU_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace mmrelu
 
@@ -434,6 +492,59 @@ int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uin
 {
     return run_strided(MMRELU_DTYPE_BF16, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, workspace,
                        workspace_bytes, stream);
+}
+
+int mmrelu_softmax_rows_f32(const float *X, float *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy, void *stream)
+{
+    return softmax_rows(4, -1, X, Y, M, N, ldx, ldy, stream);
+}
+
+int mmrelu_softmax_rows_bf16(const uint16_t *X, uint16_t *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy,
+                             void *stream)
+{
+    return softmax_rows(2, -1, X, Y, M, N, ldx, ldy, stream);
+}
+
+int mmrelu_softmax_rows_f32_variant(int32_t variant, const float *X, float *Y, int64_t M, int64_t N, int64_t ldx,
+                                    int64_t ldy, void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return softmax_rows(4, variant, X, Y, M, N, ldx, ldy, stream);
+}
+
+int mmrelu_softmax_rows_bf16_variant(int32_t variant, const uint16_t *X, uint16_t *Y, int64_t M, int64_t N,
+                                     int64_t ldx, int64_t ldy, void *stream)
+{
+    if (variant < 0) return MMRELU_ERR_INVALID_VALUE;
+    return softmax_rows(2, variant, X, Y, M, N, ldx, ldy, stream);
+}
+
+int mmrelu_softmax_rows_variant(int dtype, int64_t N, int64_t ldx, int64_t ldy, int32_t *variant)
+{
+    if (variant == nullptr) return MMRELU_ERR_NULL_POINTER;
+    if ((dtype != MMRELU_DTYPE_F32 && dtype != MMRELU_DTYPE_BF16) || N < 0 || ldx < std::max<int64_t>(1, N) ||
+        ldy < std::max<int64_t>(1, N))
+        return MMRELU_ERR_INVALID_VALUE;
+    const int esize = dtype == MMRELU_DTYPE_F32 ? 4 : 2;
+    const int64_t v = 16 / esize;
+    int32_t choice = 4;
+    if (N % v == 0 && ldx % v == 0 && ldy % v == 0) {
+        choice = 3;
+        for (int c = 2; c >= 0; --c)
+            if (N <= softmax_capacity(c, esize)) choice = c;
+    }
+    *variant = choice;
+    return MMRELU_OK;
+}
+
+int mmrelu_row_sum_f32(const float *X, float *out, int64_t M, int64_t N, int64_t ldx, void *stream)
+{
+    return row_sum_rows(4, X, out, M, N, ldx, stream);
+}
+
+int mmrelu_row_sum_bf16(const uint16_t *X, float *out, int64_t M, int64_t N, int64_t ldx, void *stream)
+{
+    return row_sum_rows(2, X, out, M, N, ldx, stream);
 }
 
 const char *mmrelu_status_string(int status)
