@@ -307,6 +307,72 @@ def layout_stats(cfg, name, steps, warmup, torch, mm, datagen):
             "tflops_b2b": round(cfg.flops / (b2b * 1e-3) / 1e12, 1)}
 
 
+ROW_WORKLOADS = [   # (op, dtype, M, N)
+    ("softmax", "f32", 8192, 8192), ("softmax", "bf16", 8192, 8192), ("softmax", "f32", 65536, 1024),
+    ("softmax", "f32", 1024, 65536), ("row_sum", "f32", 16384, 4096), ("row_sum", "bf16", 16384, 4096),
+]
+
+
+def row_stats(op, dtype, M, N, steps, warmup, torch, mm, datagen):
+    """Per-call and back-to-back times of the row softmax or row sum on an
+    M x N matrix of N(0, 2^2) values, with algorithmic bytes (one read of X,
+    plus one write of Y or of the M sums) against the HBM peak."""
+    x = datagen.normal_f32(7000 + M % 97, M, N, 2.0)
+    if dtype == "bf16":
+        x = datagen.f32_to_bf16_bits(x)
+    dx = to_device(x, torch)
+    es = 4 if dtype == "f32" else 2
+    stream = torch.cuda.current_stream()
+    if op == "softmax":
+        y = torch.empty_like(dx)
+        fn = mm.mmrelu_softmax_rows_f32 if dtype == "f32" else mm.mmrelu_softmax_rows_bf16
+        args = (dx.data_ptr(), y.data_ptr(), M, N, N, N, stream.cuda_stream)
+        kernel = f"softmax variant {mm.mmrelu_softmax_rows_variant(mm.DTYPE_F32 if dtype == 'f32' else mm.DTYPE_BF16, N, N, N)}"
+        alg = 2 * M * N * es
+    else:
+        y = torch.empty(M, dtype=torch.float32, device="cuda")
+        fn = mm.mmrelu_row_sum_f32 if dtype == "f32" else mm.mmrelu_row_sum_bf16
+        args = (dx.data_ptr(), y.data_ptr(), M, N, N, stream.cuda_stream)
+        kernel = "row_sum"
+        alg = M * N * es + 4 * M
+
+    def call():
+        rc = fn(*args)
+        if rc != mm.MMRELU_OK:
+            raise RuntimeError(mm.status_string(rc))
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return t[steps // 2], e0.elapsed_time(e1) / steps
+
+    med, b2b = timed(call)
+    r = {"op": op, "dtype": dtype, "M": M, "N": N, "kernel": kernel, "median_ms": round(med, 5),
+         "b2b_ms": round(b2b, 5), "alg_bytes": alg, "alg_gbs_b2b": round(alg / (b2b * 1e-3) / 1e9, 1),
+         "hbm_frac_b2b": round(alg / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if op == "softmax":                       # context: the framework's own fused softmax on the same tensor,
+        t_out = torch.empty_like(dx)          # and a plain copy (one read, one write: the same bytes)
+        _, tb = timed(lambda: torch.softmax(dx, dim=1, out=t_out))
+        r["torch_softmax_b2b_ms"] = round(tb, 5)
+        _, cb = timed(lambda: t_out.copy_(dx))
+        r["copy_b2b_ms"] = round(cb, 5)
+    return r
+
+
 def cpu_baseline(cfg, a, b, target_s, oracle):
     """The oracle timed on rows [0, r) of the workload, r chosen from a short
     calibration run so that the timed part takes about target_s seconds."""
@@ -354,6 +420,10 @@ def main():
                     help="instead of the benchmark line: the bf16 8192^3 and fp32 4096^3 workloads with A, B and C "
                          "stored row- or column-major (NN, TN, NT, TT, TT into a column-major C, NN into a "
                          "column-major C) through the general-stride entry points, one JSON line each")
+    ap.add_argument("--rows", action="store_true",
+                    help="instead of the benchmark line: the row softmax and row sum (the rungs before the matmul) "
+                         "on 8192 x 8192, 65536 x 1024, 1024 x 65536 and 16384 x 4096 matrices, algorithmic GB/s "
+                         "against the HBM peak, one JSON line each")
     ap.add_argument("--shapes", default="",
                     help="with --sweep: only these shapes, comma-separated dtype:MxNxK (e.g. f32:1x8192x8192)")
     ap.add_argument("--sweep-steps", type=int, default=0,
@@ -431,6 +501,20 @@ def main():
                 base = base or r["b2b_ms"]
                 r["vs_NN"] = round(r["b2b_ms"] / base, 4)
                 print(json.dumps(r), flush=True)
+        return
+
+    if args.rows:
+        import torch
+        import datagen
+        import tiled_matmul_relu_amd as mm
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        mm.load_library()
+        if args.calib_copy_mib > 0:
+            calib_copy(args.calib_copy_mib, torch)
+        for op, dtype, M, N in ROW_WORKLOADS:
+            print(json.dumps(row_stats(op, dtype, M, N, args.sweep_steps or 50, 10, torch, mm, datagen)), flush=True)
         return
 
     if args.counter_summary:

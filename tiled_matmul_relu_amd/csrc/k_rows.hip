@@ -21,7 +21,10 @@
 // accumulator over 16-byte vectors, then the wave and workgroup reduction.
 // Output is fp32 for both input dtypes.
 //
-// exp is the libm-accurate expf; 1/s is computed once per row.
+// The per-element exponential is the hardware one (__expf: exp2 of the
+// argument times log2(e) on v_exp_f32, about 2 + 1.16 |x - m| ulp); the
+// rescaling factors of the two-pass merge use the accurate expf. 1/s is
+// computed once per row.
 #include <cmath>
 #include <type_traits>
 
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kRowThreads) void softmax_regs(const T *__restrict_
     for (int e = 0; e < E; ++e)
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            v[e][i] = expf(v[e][i] - m);       // exp(-inf) = 0 for the masked entries
+            v[e][i] = __expf(v[e][i] - m);     // exp(-inf) = 0 for the masked entries
             s += v[e][i];
         }
     s = row_reduce<TPR, false>(s, red);
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kRowThreads) void softmax_online(const T *__restric
         for (int i = 1; i < V; ++i) lm = fmaxf(lm, f[i]);
         float ls = 0.0f;
 #pragma unroll
-        for (int i = 0; i < V; ++i) ls += expf(f[i] - lm);
+        for (int i = 0; i < V; ++i) ls += __expf(f[i] - lm);
         merge(m, s, lm, ls);
     }
     // Merge across the wave, then across the four waves.
@@ -230,12 +233,12 @@ __global__ __launch_bounds__(kRowThreads) void softmax_online(const T *__restric
         const int64_t c = c0 + static_cast<int64_t>(threadIdx.x) * V;
         if (c >= N) continue;
         if constexpr (V == 1) {
-            y[c] = narrow<T>(expf(widen<T>(x[c]) - m) * inv);
+            y[c] = narrow<T>(__expf(widen<T>(x[c]) - m) * inv);
         } else {
             float f[V];
             load_vec<T>(x + c, f);
 #pragma unroll
-            for (int i = 0; i < V; ++i) f[i] = expf(f[i] - m) * inv;
+            for (int i = 0; i < V; ++i) f[i] = __expf(f[i] - m) * inv;
             store_vec<T>(y + c, f);
         }
     }
