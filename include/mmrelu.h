@@ -217,15 +217,21 @@ typedef struct {
 /* Fill *out for a call of this dtype and shape. cus = 0 uses the current
  * device's compute-unit count when a device is present, else 256. Returns a
  * status as above (arguments are validated the same way, pointers aside).
- * The choice: for M <= 64 with an aligned layout, the skinny kernel of the
- * smallest row count that covers M (16, 32 or 64 rows; it splits K over the
- * eight waves of a workgroup so a 32-column strip of B streams from memory
- * once). Otherwise, among the dtype's matrix-core kernels at a large and a
- * small tile that accept the layout, the one with the least estimated time on the
- * busiest compute unit, ceil(tiles / cus) tiles times the tile's outputs
- * times the kernel's measured relative cost per output; layouts no
- * matrix-core kernel accepts use the plain tiled kernel (variant 0). The
- * launch entry points make the same choice with the device's count. */
+ * The choice, in order:
+ *   - N == 1 (a matrix-vector product): the one-wave-per-output kernel;
+ *   - an aligned layout with M <= 64 and M <= N: the skinny-M kernel of the
+ *     smallest row count that covers M (16, 32 or 64 rows; it splits K over
+ *     the eight waves of a workgroup so a 32-column strip of B streams from
+ *     memory once);
+ *   - an aligned layout with N <= 64: the skinny-N kernel of the smallest
+ *     column count that covers N (16, 32 or 64), over 32-row bands of A;
+ *   - otherwise, among the dtype's matrix-core kernels at a large and a
+ *     small tile that accept the layout, the one with the least estimated
+ *     time on the busiest compute unit, ceil(tiles / cus) tiles times the
+ *     tile's outputs times the kernel's measured relative cost per output;
+ *     layouts no matrix-core kernel accepts use the plain tiled kernel
+ *     (variant 0).
+ * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);
 

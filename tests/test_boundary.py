@@ -352,3 +352,12 @@ def test_row_ops_validate_before_launch():
     assert r(_P, 2 * _P + 2, 4, 8, 8) == mm.MMRELU_ERR_MISALIGNED          # out is fp32
     assert mm.mmrelu_row_sum_bf16(_P + 1, 2 * _P, 4, 8, 8) == mm.MMRELU_ERR_MISALIGNED
     assert r(_P, 2 * _P, 0, 8, 8) == mm.MMRELU_OK
+
+
+def test_planner_picks_gemv_for_one_column():
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        for (M, K, lda) in ((8192, 8192, 8192), (1000, 77, 80), (1, 5, 5), (4097, 2049, 2049)):
+            p = mm.mmrelu_plan(dt, M, 1, K, lda, 1, 1, cus=256)
+            assert "gemv" in p["name"] and p["block_m"] == 4 and p["grid"] == (M + 3) // 4, p
+        # two columns or more: not the gemv
+        assert "gemv" not in mm.mmrelu_plan(dt, 8192, 2, 8192, 8192, 2, 2, cus=256)["name"]

@@ -53,6 +53,9 @@ const Variant *variant_bf16_mfma128();
 // (2, 2, 2), (2, 4, 2) for skinny N.
 const Variant *variant_f32_skinny(int mb, int nb, int ks);
 const Variant *variant_bf16_skinny(int mb, int nb, int ks);
+// One wave per output (k_gemv.hip): matrix-vector products (N = 1), any layout.
+const Variant *variant_f32_gemv();
+const Variant *variant_bf16_gemv();
 
 // Strided 2-D copy (k_pack.hip): dst[r][c] = src[r][c] for r < rows, c < cols,
 // element strides (s_r, s_c) and (d_r, d_c); esize 4 or 2. Enqueues nothing

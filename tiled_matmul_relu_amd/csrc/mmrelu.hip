@@ -15,8 +15,8 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 11;
-constexpr int kNumBf16 = 11;
+constexpr int kNumF32 = 12;
+constexpr int kNumBf16 = 12;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -24,7 +24,7 @@ const Variant *const *f32_table()
                                               variant_f32_mfma64_unaligned(), variant_f32_skinny(1, 2, 1),
                                               variant_f32_skinny(2, 2, 1), variant_f32_skinny(4, 2, 2),
                                               variant_f32_skinny(2, 1, 2), variant_f32_skinny(2, 2, 2),
-                                              variant_f32_skinny(2, 4, 2)};
+                                              variant_f32_skinny(2, 4, 2), variant_f32_gemv()};
     return t;
 }
 const Variant *const *bf16_table()
@@ -34,7 +34,7 @@ const Variant *const *bf16_table()
                                                variant_bf16_mfma128(), variant_bf16_skinny(1, 2, 1),
                                                variant_bf16_skinny(2, 2, 1), variant_bf16_skinny(4, 2, 1),
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
-                                               variant_bf16_skinny(2, 4, 2)};
+                                               variant_bf16_skinny(2, 4, 2), variant_bf16_gemv()};
     return t;
 }
 
@@ -113,6 +113,9 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
 {
     static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {3, 4};
     const Variant *const *table = dtype == MMRELU_DTYPE_F32 ? f32_table() : bf16_table();
+    // A single output column is a matrix-vector product: one read of A, one
+    // wave per output (variant 11), whatever the layout.
+    if (N == 1) return 11;
     const bool fits = layout_fits(table[dtype == MMRELU_DTYPE_F32 ? 1 : 3], N, K, lda, ldb, ldc, A, B, C);
     // Skinny M or N (<= 64): the product is bound by reading the large
     // operand once, and the skinny kernels spread that read over one
