@@ -225,10 +225,14 @@ typedef struct {
  *     memory once);
  *   - an aligned layout with N <= 64: the skinny-N kernel of the smallest
  *     column count that covers N (16, 32 or 64), over 32-row bands of A;
- *   - otherwise, among the dtype's matrix-core kernels at a large and a
- *     small tile that accept the layout, the one with the least estimated
- *     time on the busiest compute unit, ceil(tiles / cus) tiles times the
- *     tile's outputs times the kernel's measured relative cost per output;
+ *   - otherwise the candidate with the least estimated time on the busiest
+ *     compute unit, ceil(tiles / cus) tiles times the tile's outputs times
+ *     the kernel's measured relative cost per output (times 1.15 for a tile
+ *     kernel left with one tile per CU, which then runs latency-bound).
+ *     Candidates: the dtype's matrix-core kernels at a large and a small
+ *     tile that accept the layout and, for aligned layouts, the six skinny
+ *     tiles, which split K over eight waves and keep every CU busy when the
+ *     large tiles cannot (small squares, long K with few output tiles);
  *     layouts no matrix-core kernel accepts use the plain tiled kernel
  *     (variant 0).
  * The launch entry points make the same choice with the device's count. */

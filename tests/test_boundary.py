@@ -100,7 +100,8 @@ def test_planner_picks_skinny_kernels_for_few_rows():
         for M, rows in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
             p = mm.mmrelu_plan(dt, M, 8192, 8192, 8192, 8192, 8192, cus=256)
             assert "skinny" in p["name"] and p["block_m"] == rows and p["grid"] == 8192 // 32, (M, p["name"])
-        assert "skinny" not in mm.mmrelu_plan(dt, 65, 8192, 8192, 8192, 8192, 8192, cus=256)["name"]
+        # past 64 rows the cost model decides (not the few-rows rule)
+        assert mm.mmrelu_plan(dt, 65, 8192, 8192, 8192, 8192, 8192, cus=256)["block_m"] != 64
         # an odd leading dimension needs a kernel that accepts any layout
         p = mm.mmrelu_plan(dt, 16, 8191, 8192, 8192, 8191, 8191, cus=256)
         assert "skinny" not in p["name"]
@@ -113,7 +114,9 @@ def test_planner_picks_skinny_kernels_for_few_columns():
             p = mm.mmrelu_plan(dt, 8192, N, 8192, 8192, N, N, cus=256)
             assert "skinny" in p["name"] and p["block_n"] == cols and p["block_m"] == 32, (N, p["name"])
             assert p["grid"] == 8192 // 32
-        assert "skinny" not in mm.mmrelu_plan(dt, 8192, 72, 8192, 8192, 72, 72, cus=256)["name"]
+        # past 64 columns the cost model decides among all candidates
+        p = mm.mmrelu_plan(dt, 8192, 72, 8192, 8192, 72, 72, cus=256)
+        assert p["grid"] == ((8192 + p["block_m"] - 1) // p["block_m"]) * ((72 + p["block_n"] - 1) // p["block_n"])
         # both small: the smaller dimension decides
         assert mm.mmrelu_plan(dt, 16, 64, 8192, 8192, 64, 64, cus=256)["block_m"] == 16
         p = mm.mmrelu_plan(dt, 64, 16, 8192, 8192, 16, 16, cus=256)
@@ -182,26 +185,27 @@ def test_planner_tile_choice_by_wave_quantization():
     """Smaller tiles when the large tile's grid leaves CUs idle (the a7 rule:
     ceil(tiles / CUs) * tile outputs * measured relative cost)."""
     sq = lambda dt, n, cus=256: mm.mmrelu_plan(dt, n, n, n, n, n, n, cus=cus)
-    # fp32: 256^3 and 1024^3 fit one 64x64 tile per CU; 4096^3 fills the CUs with 128x128
-    for n, tile in ((256, 64), (1024, 64), (4096, 128)):
+    # fp32: 2048^3 takes 64x64 tiles (four per CU: 4 * 4096 * 1.02 against one
+    # 128x128 tile per CU at 16384 * 1.15); 4096^3 and up fill the CUs with 128x128
+    for n, tile in ((2048, 64), (4096, 128), (8192, 128)):
         p = sq(mm.DTYPE_F32, n)
-        assert (p["block_m"], p["block_n"]) == (tile, tile) and "unaligned" not in p["name"], (n, p["name"])
+        assert (p["block_m"], p["block_n"]) == (tile, tile) and "mfma" in p["name"], (n, p["name"])
+        assert "unaligned" not in p["name"]
     # the ragged shape: 792 tiles of 128x128 (4 on the busiest CU, 4 * 16384 outputs)
     # against 3055 of 64x64 (12 on the busiest CU, 12 * 4096 * 1.02)
     p = mm.mmrelu_plan(mm.DTYPE_F32, 4097, 3001, 2049, 2049, 3001, 3001, cus=256)
     assert "unaligned" in p["name"] and p["block_m"] == 64 and p["grid"] == 65 * 47
-    # bf16: 128x128 while the 256x256 grid has at most one tile per CU and the
-    # small grid too (1024^2, 2048^2); 256x256 from 3072^2 on
-    for n, tile in ((1024, 128), (2048, 128), (3072, 256), (4096, 256), (6144, 256), (8192, 256)):
+    # bf16: 128x128 at 2048^2 (one tile per CU on either grid); 256x256 from 3072^2 on
+    for n, tile in ((2048, 128), (3072, 256), (4096, 256), (6144, 256), (8192, 256)):
         p = sq(mm.DTYPE_BF16, n)
-        assert p["block_m"] == tile, (n, p["name"])
+        assert p["block_m"] == tile and "skinny" not in p["name"], (n, p["name"])
     assert "pingpong" in sq(mm.DTYPE_BF16, 8192)["name"]
     # fewer CUs shift the crossover: on 64 CUs 2048^2 bf16 has one 256x256 tile per CU
     assert sq(mm.DTYPE_BF16, 2048, cus=64)["block_m"] == 256
     # the plan's kernel is the one the launch uses: planning with any CU count
     # stays within the candidates that accept the layout
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1000, 1000, 1000, 1000, 1000, cus=256)
-    assert "mfma" in p["name"] or "pingpong" in p["name"]
+    assert "mfma" in p["name"] or "pingpong" in p["name"] or "skinny" in p["name"]
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1001, 1000, 1000, 1001, 1001, cus=256)
     assert "simple" in p["name"]
 
@@ -361,3 +365,26 @@ def test_planner_picks_gemv_for_one_column():
             assert "gemv" in p["name"] and p["block_m"] == 4 and p["grid"] == (M + 3) // 4, p
         # two columns or more: not the gemv
         assert "gemv" not in mm.mmrelu_plan(dt, 8192, 2, 8192, 8192, 2, 2, cus=256)["name"]
+
+
+def test_planner_cost_model_uses_skinny_tiles_where_large_tiles_idle_cus():
+    """The K-split skinny tiles enter the cost model (relative costs fitted
+    to measured times): small squares and long-K products with few output
+    tiles take them, large squares keep the tile kernels."""
+    plan = lambda dt, M, N, K: mm.mmrelu_plan(dt, M, N, K, K, N, N, cus=256)
+    F, B = mm.DTYPE_F32, mm.DTYPE_BF16
+    expect = {
+        (F, 256, 256, 256): "skinny", (F, 512, 512, 8192): "skinny<float,32x32,ks2>",
+        (F, 1024, 1024, 8192): "skinny<float,32x64,ks2>", (F, 128, 4096, 4096): "skinny<float,32x64,ks2>",
+        (F, 256, 8192, 1024): "f32_mfma<64,64", (F, 4096, 4096, 4096): "f32_mfma<128,128",
+        (B, 256, 256, 256): "skinny", (B, 512, 512, 8192): "skinny<bf16,32x32,ks2>",
+        (B, 1024, 1024, 1024): "skinny<bf16,32x64,ks2>", (B, 4096, 128, 4096): "skinny<bf16,32x64,ks2>",
+        (B, 256, 8192, 1024): "bf16_mfma<128,128", (B, 2048, 2048, 2048): "bf16_mfma<128,128",
+        (B, 4096, 4096, 4096): "pingpong", (B, 8192, 8192, 8192): "pingpong",
+    }
+    for (dt, M, N, K), want in expect.items():
+        name = plan(dt, M, N, K)["name"]
+        assert want in name, ((M, N, K), name)
+    # unaligned layouts keep the tile kernels (the skinny ones need 16-byte rows)
+    p = mm.mmrelu_plan(F, 512, 511, 8192, 8192, 511, 511, cus=256)
+    assert "unaligned" in p["name"]

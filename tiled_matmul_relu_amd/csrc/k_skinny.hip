@@ -317,7 +317,14 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 
 // Skinny-M tiles (16, 32 or 64 rows by 32 columns) and skinny-N tiles (32
 // rows by 16, 32 or 64 columns). Any shape is covered by a grid of tiles;
-// the planner uses them where one dimension is small. Each uses the k depth
+// the planner uses them where one dimension is small, and through its cost
+// model where the large tiles would leave CUs idle. Their relative cost per
+// output (against the dtype's fastest tile kernel at full occupancy) was
+// fitted on 256^3 .. 2048^3, 512 x 512 x 8192, 1024 x 1024 x 8192 and
+// 128 / 4096-row products: about 1.04 - 1.1 in fp32, 5.3 - 9.5 in bf16 (the
+// bf16 ping-pong kernel does far more per output at full occupancy); the
+// 16-wide tiles, slower per output, are priced up so that the planner uses
+// them only through the few-rows and few-columns rules. Each uses the k depth
 // per slab (KS) and ring depth measured fastest for its role at 8192 x 8192:
 // two stages (one slab in flight) throughout, since deeper rings read HBM
 // more slowly here (fp32 1 x 8192 x 8192: 39 us with two stages, 48 us with
@@ -326,17 +333,17 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 const Variant *variant_f32_skinny(int mb, int nb, int ks)
 {
     static const Variant m1 = {"mmrelu_skinny<float,16x32,ks1>", MMRELU_DTYPE_F32, 16, 32, 16, kThreads, 1, 4,
-                               launch_skinny<float, 1, 2, 1, 2>, 1.0f};
+                               launch_skinny<float, 1, 2, 1, 2>, 2.3f};
     static const Variant m2 = {"mmrelu_skinny<float,32x32,ks1>", MMRELU_DTYPE_F32, 32, 32, 16, kThreads, 1, 4,
-                               launch_skinny<float, 2, 2, 1, 2>, 1.0f};
+                               launch_skinny<float, 2, 2, 1, 2>, 1.1f};
     static const Variant m4 = {"mmrelu_skinny<float,64x32,ks2>", MMRELU_DTYPE_F32, 64, 32, 32, kThreads, 1, 4,
-                               launch_skinny<float, 4, 2, 2, 2>, 1.0f};
+                               launch_skinny<float, 4, 2, 2, 2>, 1.05f};
     static const Variant n1 = {"mmrelu_skinny<float,32x16,ks2>", MMRELU_DTYPE_F32, 32, 16, 32, kThreads, 1, 4,
-                               launch_skinny<float, 2, 1, 2, 2>, 1.0f};
+                               launch_skinny<float, 2, 1, 2, 2>, 2.3f};
     static const Variant n2 = {"mmrelu_skinny<float,32x32,ks2>", MMRELU_DTYPE_F32, 32, 32, 32, kThreads, 1, 4,
-                               launch_skinny<float, 2, 2, 2, 2>, 1.0f};
+                               launch_skinny<float, 2, 2, 2, 2>, 1.08f};
     static const Variant n4 = {"mmrelu_skinny<float,32x64,ks2>", MMRELU_DTYPE_F32, 32, 64, 32, kThreads, 1, 4,
-                               launch_skinny<float, 2, 4, 2, 2>, 1.0f};
+                               launch_skinny<float, 2, 4, 2, 2>, 1.04f};
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : &m2;
     if (nb == 2 && mb == 4) return &m4;
     return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
@@ -344,17 +351,17 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
 const Variant *variant_bf16_skinny(int mb, int nb, int ks)
 {
     static const Variant m1 = {"mmrelu_skinny<bf16,16x32,ks1>", MMRELU_DTYPE_BF16, 16, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 1, 2, 1, 2>, 1.0f};
+                               launch_skinny<uint16_t, 1, 2, 1, 2>, 9.5f};
     static const Variant m2 = {"mmrelu_skinny<bf16,32x32,ks1>", MMRELU_DTYPE_BF16, 32, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 2, 1, 2>, 1.0f};
+                               launch_skinny<uint16_t, 2, 2, 1, 2>, 9.5f};
     static const Variant m4 = {"mmrelu_skinny<bf16,64x32,ks1>", MMRELU_DTYPE_BF16, 64, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 4, 2, 1, 2>, 1.0f};
+                               launch_skinny<uint16_t, 4, 2, 1, 2>, 6.0f};
     static const Variant n1 = {"mmrelu_skinny<bf16,32x16,ks2>", MMRELU_DTYPE_BF16, 32, 16, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 1, 2, 2>, 1.0f};
+                               launch_skinny<uint16_t, 2, 1, 2, 2>, 9.5f};
     static const Variant n2 = {"mmrelu_skinny<bf16,32x32,ks2>", MMRELU_DTYPE_BF16, 32, 32, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 2, 2, 2>, 1.0f};
+                               launch_skinny<uint16_t, 2, 2, 2, 2>, 9.0f};
     static const Variant n4 = {"mmrelu_skinny<bf16,32x64,ks2>", MMRELU_DTYPE_BF16, 32, 64, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 4, 2, 2>, 1.0f};
+                               launch_skinny<uint16_t, 2, 4, 2, 2>, 5.3f};
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;
     return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
 }
