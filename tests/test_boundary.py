@@ -172,9 +172,10 @@ def test_plans_for_the_workloads():
     # 8192^3 bf16: matrix-core kernel, whole waves
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 8192, 8192, 8192, 8192, 8192, 8192, cus=256)
     assert "bf16_pingpong" in p["name"] and p["idle_slots_last"] == 0
-    # bf16 with an odd leading dimension falls back to the plain tiled kernel
+    # bf16 with N, K or a leading dimension off the 8-element grid: the
+    # any-layout matrix-core kernel
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 100, 100, 100, 100, 100, 100, cus=256)
-    assert "simple" in p["name"]
+    assert "bf16_any" in p["name"] and p["grid"] == 4
     with pytest.raises(mm.MmreluError):
         mm.mmrelu_plan(mm.DTYPE_F32, -1, 4, 4, 4, 4, 4)
     with pytest.raises(mm.MmreluError):
@@ -207,7 +208,25 @@ def test_planner_tile_choice_by_wave_quantization():
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1000, 1000, 1000, 1000, 1000, cus=256)
     assert "mfma" in p["name"] or "pingpong" in p["name"] or "skinny" in p["name"]
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1001, 1000, 1000, 1001, 1001, cus=256)
-    assert "simple" in p["name"]
+    assert "bf16_any" in p["name"]
+
+
+def test_planner_any_layout_tile():
+    """Unaligned bf16: 128x128 tiles once their grid gives every CU two or
+    more, else 64x64 tiles."""
+    plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
+    # 4097 x 3001: 33 * 24 = 792 tiles of 128x128 (>= 512)
+    assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_any<128,128,32>"
+    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
+    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU
+    p = plan(2047, 2047, 2047)
+    assert p["name"] == "mmrelu_bf16_any<64,64,32>" and p["grid"] == 32 * 32
+    assert plan(1001, 1001, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
+    # the threshold moves with the CU count: 2047^2 on 128 CUs takes 128x128
+    assert plan(2047, 2047, 2047, cus=128)["name"] == "mmrelu_bf16_any<128,128,32>"
+    # just at the threshold: 32 x 16 = 512 tiles
+    assert plan(4096, 2047, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
+    assert plan(4096 - 128, 2047, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
 
 
 def test_every_variant_plans():

@@ -53,6 +53,8 @@ const Variant *variant_bf16_mfma128();
 // (2, 2, 2), (2, 4, 2) for skinny N.
 const Variant *variant_f32_skinny(int mb, int nb, int ks);
 const Variant *variant_bf16_skinny(int mb, int nb, int ks);
+// bf16 matrix-core kernel for any layout (k_bf16_any.hip).
+const Variant *variant_bf16_any(int bt);   // bt = 64 or 128
 // One wave per output (k_gemv.hip): matrix-vector products (N = 1), any layout.
 const Variant *variant_f32_gemv();
 const Variant *variant_bf16_gemv();
