@@ -230,13 +230,13 @@ typedef struct {
  *     the kernel's measured relative cost per output (times 1.15 for a tile
  *     kernel left with one tile per CU, which then runs latency-bound).
  *     Candidates: the dtype's matrix-core kernels at a large and a small
- *     tile that accept the layout and, for aligned layouts, the six skinny
- *     tiles, which split K over eight waves and keep every CU busy when the
- *     large tiles cannot (small squares, long K with few output tiles);
- *     other layouts run the fp32 unaligned matrix-core kernels, or for
- *     bf16 the any-layout matrix-core kernel: 128 x 128 tiles (variant 13)
- *     when that grid gives every CU at least two tiles, else 64 x 64 tiles
- *     (variant 12).
+ *     tile that accept the layout and, for aligned layouts, the seven
+ *     skinny tiles (variants 5 - 10 and the 64 x 64 variant 12), which split
+ *     K over eight waves and keep every CU busy when the large tiles cannot
+ *     (small squares, long K with few output tiles); other layouts run the
+ *     fp32 unaligned matrix-core kernels, or for bf16 the any-layout
+ *     matrix-core kernel: 128 x 128 tiles (variant 14) when that grid gives
+ *     every CU at least two tiles, else 64 x 64 tiles (variant 13).
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);

@@ -100,8 +100,10 @@ def test_planner_picks_skinny_kernels_for_few_rows():
         for M, rows in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
             p = mm.mmrelu_plan(dt, M, 8192, 8192, 8192, 8192, 8192, cus=256)
             assert "skinny" in p["name"] and p["block_m"] == rows and p["grid"] == 8192 // 32, (M, p["name"])
-        # past 64 rows the cost model decides (not the few-rows rule)
-        assert mm.mmrelu_plan(dt, 65, 8192, 8192, 8192, 8192, 8192, cus=256)["block_m"] != 64
+        # past 64 rows the cost model decides, not the few-rows rule's 64 x 32
+        # strips (fp32: 32 x 32 tiles, three row tiles; bf16: 64 x 64 tiles)
+        p = mm.mmrelu_plan(dt, 65, 8192, 8192, 8192, 8192, 8192, cus=256)
+        assert p["variant"] != 7 and p["variant"] == (9 if dt == mm.DTYPE_F32 else 12), p["name"]
         # an odd leading dimension needs a kernel that accepts any layout
         p = mm.mmrelu_plan(dt, 16, 8191, 8192, 8192, 8191, 8191, cus=256)
         assert "skinny" not in p["name"]
@@ -209,6 +211,21 @@ def test_planner_tile_choice_by_wave_quantization():
     assert "mfma" in p["name"] or "pingpong" in p["name"] or "skinny" in p["name"]
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 1000, 1001, 1000, 1000, 1001, 1001, cus=256)
     assert "bf16_any" in p["name"]
+
+
+def test_planner_square_skinny_tile():
+    """The 64x64 skinny tile (variant 12) wins small squares and long-K
+    products with 256 or fewer output tiles of 64x64; larger grids go back to
+    the tile kernels, smaller ones to narrower skinny tiles."""
+    plan = lambda dt, m, n, k: mm.mmrelu_plan(dt, m, n, k, k, n, n, cus=256)
+    for dt in (mm.DTYPE_F32, mm.DTYPE_BF16):
+        assert plan(dt, 1024, 1024, 1024)["variant"] == 12
+        assert plan(dt, 1024, 1024, 8192)["variant"] == 12
+        assert plan(dt, 2048, 2048, 2048)["variant"] in (3, 4)      # the 64x64 / 128x128 tile kernels
+        assert plan(dt, 512, 512, 8192)["name"].startswith("mmrelu_skinny") and plan(dt, 512, 512, 8192)["block_m"] == 32
+    assert plan(mm.DTYPE_F32, 768, 768, 768)["block_m"] == 32       # 576 tiles of 32x32
+    p = mm.mmrelu_plan_variant(mm.DTYPE_F32, 12, 1000, 264, 512, 512, 264, 264, cus=256)
+    assert (p["block_m"], p["block_n"], p["grid"]) == (64, 64, 16 * 5)
 
 
 def test_planner_any_layout_tile():
@@ -394,10 +411,11 @@ def test_planner_cost_model_uses_skinny_tiles_where_large_tiles_idle_cus():
     F, B = mm.DTYPE_F32, mm.DTYPE_BF16
     expect = {
         (F, 256, 256, 256): "skinny", (F, 512, 512, 8192): "skinny<float,32x32,ks2>",
-        (F, 1024, 1024, 8192): "skinny<float,32x64,ks2>", (F, 128, 4096, 4096): "skinny<float,32x64,ks2>",
+        (F, 1024, 1024, 8192): "skinny<float,64x64,ks2>", (F, 128, 4096, 4096): "skinny<float,32x64,ks2>",
         (F, 256, 8192, 1024): "f32_mfma<64,64", (F, 4096, 4096, 4096): "f32_mfma<128,128",
         (B, 256, 256, 256): "skinny", (B, 512, 512, 8192): "skinny<bf16,32x32,ks2>",
-        (B, 1024, 1024, 1024): "skinny<bf16,32x64,ks2>", (B, 4096, 128, 4096): "skinny<bf16,32x64,ks2>",
+        (B, 1024, 1024, 1024): "skinny<bf16,64x64,ks2>", (B, 4096, 128, 4096): "skinny<bf16,32x64,ks2>",
+        (B, 128, 8192, 8192): "skinny<bf16,64x64,ks2>", (B, 256, 4096, 4096): "skinny<bf16,64x64,ks2>",
         (B, 256, 8192, 1024): "bf16_mfma<128,128", (B, 2048, 2048, 2048): "bf16_mfma<128,128",
         (B, 4096, 4096, 4096): "pingpong", (B, 8192, 8192, 8192): "pingpong",
     }

@@ -21,7 +21,7 @@ import tiled_matmul_relu_amd as mm
 
 pytestmark = pytest.mark.gpu
 
-SKINNY = [5, 6, 7, 8, 9, 10]  # tiles 16x32, 32x32, 64x32 (few rows), 32x16, 32x32, 32x64 (few columns)
+SKINNY = [5, 6, 7, 8, 9, 10, 12]  # tiles 16x32, 32x32, 64x32 (few rows), 32x16, 32x32, 32x64 (few columns), 64x64
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:

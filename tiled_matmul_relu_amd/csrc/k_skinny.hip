@@ -11,10 +11,13 @@
 //    by NB = 2 column blocks for skinny M (a 32-column strip of B per
 //    workgroup, 256 workgroups at N = 8192), MB = 2 by NB = 1, 2, 4 for
 //    skinny N (a 32-row band of A per workgroup). The small operand is read
-//    by every workgroup and stays in L2.
+//    by every workgroup and stays in L2. A 64 x 64 tile (MB = NB = 4) serves
+//    small squares and long-K products with few output tiles, where it
+//    halves the operand bytes per output of the 32 x 64 tile.
 //  * Its eight waves split K into eight contiguous ranges of slabs and run
 //    independently, with no barrier inside the loop; the partial tiles are
-//    summed through LDS at the end (fixed order: deterministic results).
+//    summed through LDS at the end (fixed order: deterministic results), one
+//    16 x 16 block per wave (two at 64 x 64).
 //  * Both operands are issued kDepth slabs ahead of the slab being
 //    multiplied: A fragments straight into registers (each lane's 8 bf16 /
 //    4 fp32 of a row are contiguous), rotating through kDepth + 1 register
@@ -88,7 +91,7 @@ struct SkinnyShape {
     static constexpr int kLdsBytes = kRingBytes > kRedBytes ? kRingBytes : kRedBytes;
     static_assert(kBlkK * kRowBytes == NB * 1024, "one 1 KB copy per 16 columns and k block");
     static_assert(kStages >= 2, "ring depth");
-    static_assert(MB * NB <= kWaves, "one reducing wave per 16 x 16 block");
+    static_assert(MB * NB <= kWaves || (MB * NB) % kWaves == 0, "whole blocks per reducing wave");
     static_assert(kDepth * KS * (NB + MB) <= 63, "vmcnt range");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -257,51 +260,55 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     __syncthreads();
 
     // Sum the eight waves' partial tiles: wave w writes block b of lane l at
-    // ((w * kNBlk + b) * 64 + l) * 16 bytes; wave q < kNBlk then reduces
-    // block q over the waves in order.
+    // ((w * kNBlk + b) * 64 + l) * 16 bytes; the reducing wave of block b
+    // then adds them over the waves in order.
     f32x4 *red = reinterpret_cast<f32x4 *>(lds);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) red[(wave * kNBlk + i * NB + jb) * 64 + lane] = acc[i][jb];
     __syncthreads();
-    if (wave >= kNBlk) return;
-    f32x4 v = red[wave * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += red[(w * kNBlk + wave) * 64 + lane];
-    const int i = wave / NB, jb = wave % NB;
-    const int row = 16 * i + t;                        // within the tile
-    const int col = 16 * jb + 4 * g;
-
-    // Epilogue: bias of the lane's four columns (only when there is one),
-    // activation, one masked store of four consecutive columns.
-    float bj[4];
-    if (bias != nullptr) {
-        const __amdgpu_buffer_rsrc_t rbias = make_bias_rsrc(bias, n0, N, kEsize);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            bj[r] = std::is_same_v<T, uint16_t> ? bias_bf16(rbias, col + r) : bias_f32(rbias, col + r);
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bj[r] = 0.0f;
-    }
+    // Wave w reduces blocks w, w + 8, ... (one block per wave up to 32 x 64
+    // tiles, two at 64 x 64).
     const __amdgpu_buffer_rsrc_t rc =
         make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0, ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * kEsize);
-    const uint32_t off = (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * kEsize) : kOutOfRange;
-    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
-        constexpr int ACT = decltype(act_c)::value;
-        if constexpr (std::is_same_v<T, uint16_t>) {
-            bf16x4 o;
+    for (int b = wave; b < kNBlk; b += kWaves) {
+        f32x4 v = red[b * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[r]));
-            store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+        for (int w = 1; w < kWaves; ++w) v += red[(w * kNBlk + b) * 64 + lane];
+        const int i = b / NB, jb = b % NB;
+        const int row = 16 * i + t;                    // within the tile
+        const int col = 16 * jb + 4 * g;
+
+        // Epilogue: bias of the lane's four columns (only when there is one),
+        // activation, one masked store of four consecutive columns.
+        float bj[4];
+        if (bias != nullptr) {
+            const __amdgpu_buffer_rsrc_t rbias = make_bias_rsrc(bias, n0, N, kEsize);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                bj[r] = std::is_same_v<T, uint16_t> ? bias_bf16(rbias, col + r) : bias_f32(rbias, col + r);
         } else {
-            f32x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = activate<ACT>(v[r] + bj[r]);
-            store_b128(rc, off, __builtin_bit_cast(u32x4, o));
+            for (int r = 0; r < 4; ++r) bj[r] = 0.0f;
         }
-    });
+        const uint32_t off =
+            (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * kEsize) : kOutOfRange;
+        with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(act_c)::value;
+            if constexpr (std::is_same_v<T, uint16_t>) {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[r]));
+                store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+            } else {
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = activate<ACT>(v[r] + bj[r]);
+                store_b128(rc, off, __builtin_bit_cast(u32x4, o));
+            }
+        });
+    }
 }
 
 template <typename T, int MB, int NB, int KS, int STAGES>
@@ -315,8 +322,11 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 
 }  // namespace
 
-// Skinny-M tiles (16, 32 or 64 rows by 32 columns) and skinny-N tiles (32
-// rows by 16, 32 or 64 columns). Any shape is covered by a grid of tiles;
+// Skinny-M tiles (16, 32 or 64 rows by 32 columns), skinny-N tiles (32
+// rows by 16, 32 or 64 columns) and the 64 x 64 tile (relative cost 1.03
+// fp32, 4.5 bf16: measured 1024^3 fp32 25.7 against 27.5 us on 32 x 64
+// tiles, bf16 10.0 against 12.7; 1024 x 1024 x 8192 bf16 48.6 against 65).
+// Any shape is covered by a grid of tiles;
 // the planner uses them where one dimension is small, and through its cost
 // model where the large tiles would leave CUs idle. Their relative cost per
 // output (against the dtype's fastest tile kernel at full occupancy) was
@@ -344,6 +354,9 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
                                launch_skinny<float, 2, 2, 2, 2>, 1.08f};
     static const Variant n4 = {"mmrelu_skinny<float,32x64,ks2>", MMRELU_DTYPE_F32, 32, 64, 32, kThreads, 1, 4,
                                launch_skinny<float, 2, 4, 2, 2>, 1.04f};
+    static const Variant sq = {"mmrelu_skinny<float,64x64,ks2>", MMRELU_DTYPE_F32, 64, 64, 32, kThreads, 1, 4,
+                               launch_skinny<float, 4, 4, 2, 2>, 1.03f};
+    if (nb == 4 && mb == 4) return &sq;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : &m2;
     if (nb == 2 && mb == 4) return &m4;
     return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
@@ -362,6 +375,9 @@ const Variant *variant_bf16_skinny(int mb, int nb, int ks)
                                launch_skinny<uint16_t, 2, 2, 2, 2>, 9.0f};
     static const Variant n4 = {"mmrelu_skinny<bf16,32x64,ks2>", MMRELU_DTYPE_BF16, 32, 64, 64, kThreads, 1, 8,
                                launch_skinny<uint16_t, 2, 4, 2, 2>, 5.3f};
+    static const Variant sq = {"mmrelu_skinny<bf16,64x64,ks2>", MMRELU_DTYPE_BF16, 64, 64, 64, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 4, 4, 2, 2>, 4.5f};
+    if (nb == 4 && mb == 4) return &sq;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;
     return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
 }

@@ -15,8 +15,8 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 12;
-constexpr int kNumBf16 = 14;
+constexpr int kNumF32 = 13;
+constexpr int kNumBf16 = 15;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -24,7 +24,8 @@ const Variant *const *f32_table()
                                               variant_f32_mfma64_unaligned(), variant_f32_skinny(1, 2, 1),
                                               variant_f32_skinny(2, 2, 1), variant_f32_skinny(4, 2, 2),
                                               variant_f32_skinny(2, 1, 2), variant_f32_skinny(2, 2, 2),
-                                              variant_f32_skinny(2, 4, 2), variant_f32_gemv()};
+                                              variant_f32_skinny(2, 4, 2), variant_f32_gemv(),
+                                              variant_f32_skinny(4, 4, 2)};
     return t;
 }
 const Variant *const *bf16_table()
@@ -35,7 +36,8 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 2, 1), variant_bf16_skinny(4, 2, 1),
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
-                                               variant_bf16_any(64), variant_bf16_any(128)};
+                                               variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
+                                               variant_bf16_any(128)};
     return t;
 }
 
@@ -108,7 +110,7 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
 // full tiles of block_m x block_n outputs at the variant's measured relative
 // cost per output (wave quantisation of the grid over the CUs). bf16
 // layouts the 16-byte-vector kernels do not accept go to the any-layout
-// matrix-core kernel (variants 12 and 13); the plain tiled kernel (variant 0) is
+// matrix-core kernel (variants 13 and 14); the plain tiled kernel (variant 0) is
 // only reached through the _variant entry points.
 // Pointers are taken as 16-byte aligned when null (planning without buffers).
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -136,17 +138,18 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     if (dtype == MMRELU_DTYPE_F32) cand = fits ? f32_aligned : f32_any;
     else if (fits) cand = bf16_aligned;
     else {
-        // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 13)
+        // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 14)
         // once their grid gives every CU two or more, else 64 x 64 tiles
-        // (variant 12); with one such workgroup per CU the larger tile runs
+        // (variant 13); with one such workgroup per CU the larger tile runs
         // slower than four smaller ones (measured: 2047^3, 104 against 95 us;
         // 8191^2 x 1001, 0.51 against 0.64 ms).
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        return tiles128 >= 2 * static_cast<int64_t>(cus) ? 13 : 12;
+        return tiles128 >= 2 * static_cast<int64_t>(cus) ? 14 : 13;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
-    // six skinny tiles, which split K over eight waves and so keep every CU
-    // busy when the large tiles would leave most of them idle. A tile kernel
+    // seven skinny tiles (variants 5 - 10 and 12), which split K over eight
+    // waves and so keep every CU busy when the large tiles would leave most
+    // of them idle. A tile kernel
     // with a single tile per CU runs four waves per CU and is latency-bound:
     // its estimate carries a factor 1.15 (measured: 1024 x 1024 x 8192 fp32,
     // 185 us on 64x64 tiles against 159 us on 32x64 skinny tiles).
@@ -166,8 +169,10 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     };
     consider(cand[0], true);
     consider(cand[1], true);
-    if (fits)
+    if (fits) {
         for (int32_t v = 5; v <= 10; ++v) consider(v, false);
+        consider(12, false);
+    }
     if (best < 0) best = cand[0];
     return best;
 }
