@@ -112,17 +112,21 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, t = lane & 15;
 
-    // Tile of this workgroup, row-major over the (tiles_m x tiles_n) grid.
-    // bf16 with several column strips: consecutive strips on one XCD. A bf16
-    // 32-column strip row is 64 bytes, half of a 128-byte line, and the
-    // neighbouring strip reads the other half; on the same XCD the two share
-    // one L2 fill instead of each fetching the line. Otherwise the dispatch
-    // order, which spreads the tiles that run together over more HBM channels
-    // (measured: fp32 8192 x 8192 B at M <= 16 reads 10% faster that way).
+    // Tile of this workgroup. bf16: each XCD takes a contiguous range of
+    // tiles, walked in bands of up to eight tile rows, column by column, so
+    // the tiles that share a strip of B (or a band of A) run on one XCD and
+    // its L2 serves the operand once (measured: 128 x 8192 x 8192, 53.4 ->
+    // 47.1 us; 256 x 4096 x 4096, 30.4 -> 26.6; 8192 x 64 x 8192, 31.1 ->
+    // 28.8). A bf16 32-column strip row is also only 64 bytes, half of a
+    // 128-byte line, and the neighbouring strip reads the other half; on the
+    // same XCD the two share one L2 fill. fp32 keeps the dispatch order,
+    // which spreads the tiles that run together over more HBM channels
+    // (measured: fp32 8192 x 8192 B at M <= 16 reads 10% faster that way, and
+    // the grouped order gained nothing on the shapes above).
     const int tiles_n = (N + 16 * NB - 1) / (16 * NB);
     int tm, tn;
-    if (sizeof(T) == 2 && tiles_n > 1) {
-        tile_of(blockIdx.x, gridDim.x, (M + 16 * MB - 1) / (16 * MB), tiles_n, 1, tm, tn);
+    if (sizeof(T) == 2) {
+        tile_of(blockIdx.x, gridDim.x, (M + 16 * MB - 1) / (16 * MB), tiles_n, 8, tm, tn);
     } else {
         tm = blockIdx.x / tiles_n;
         tn = blockIdx.x % tiles_n;
