@@ -468,6 +468,8 @@ def main():
             # between skinny and square: few output tiles, long K; and the
             # ragged shape (odd leading dimensions)
             shapes += [(128, 8192, 8192), (256, 4096, 4096), (512, 512, 8192), (1024, 1024, 8192), (4097, 3001, 2049)]
+            # one GPU's share of an 8-way split of C by rows: 4096^3 fp32, 8192^3 bf16
+            shapes += [(512, 4096, 4096) if dtype == "f32" else (1024, 8192, 8192)]
             todo += [(dtype, s) for s in shapes]
         if args.shapes:
             todo = []
