@@ -1,8 +1,10 @@
 """Build libmmrelu.so (the gfx950 HIP library) in-tree with hipcc.
 
 Each ``csrc/*.hip`` file is compiled to an object in parallel, then linked
-into ``tiled_matmul_relu_amd/libmmrelu.so``. Run ``python -m
-tiled_matmul_relu_amd.build`` or call ``build()``.
+into ``tiled_matmul_relu_amd/libmmrelu.so``. The C example
+(``examples/mmrelu_run.c``, the library used from C without Python) is then
+built with gcc against the library into ``_build/mmrelu_run``. Run ``python
+-m tiled_matmul_relu_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmmrelu.so")
 OBJDIR = os.path.join(PKG, "_build")
+EXAMPLE = os.path.join(OBJDIR, "mmrelu_run")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -71,7 +75,25 @@ def build(jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_example()
     return LIB
+
+
+def build_example() -> str:
+    """Strict C99 with the HIP runtime headers as system headers; the binary
+    finds libmmrelu.so next to its own directory's parent ($ORIGIN/..)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C example")
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(ROOT, 'include')}", "-isystem", os.path.join(ROCM, "include"),
+           os.path.join(PKG, "examples", "mmrelu_run.c"), "-o", EXAMPLE, f"-L{PKG}", "-lmmrelu",
+           f"-L{os.path.join(ROCM, 'lib')}", "-lamdhip64", "-Wl,-rpath,$ORIGIN/..",
+           f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("C example build failed:\n" + r.stdout + r.stderr)
+    return EXAMPLE
 
 
 if __name__ == "__main__":
