@@ -34,7 +34,11 @@
  *   MMRELU_ERR_NULL_POINTER   C null (M, N > 0), or A/B null (M, N, K > 0).
  *   MMRELU_ERR_MISALIGNED     a pointer not aligned to its element size.
  *   MMRELU_ERR_LAUNCH         the HIP launch itself failed (hipGetLastError);
- *                             e.g. the current device is not a gfx950.
+ *                             e.g. the current device is not a gfx950. The
+ *                             check also returns (and clears) an error that
+ *                             an earlier HIP call on the same thread left
+ *                             pending, so callers should check their own HIP
+ *                             calls before calling the library.
  * Empty outputs (M == 0 or N == 0) return MMRELU_OK without a launch; K == 0
  * writes C = 0 (the K loop runs zero times and relu(0) is stored).
  *
