@@ -240,7 +240,7 @@ typedef struct {
  *     (small squares, long K with few output tiles); other layouts run the
  *     fp32 unaligned matrix-core kernels, or for bf16 the any-layout
  *     matrix-core kernel: 128 x 128 tiles (variant 14) when that grid gives
- *     every CU at least two tiles, else 64 x 64 tiles (variant 13).
+ *     every CU at least one tile, else 64 x 64 tiles (variant 13).
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);

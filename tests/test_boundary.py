@@ -229,21 +229,22 @@ def test_planner_square_skinny_tile():
 
 
 def test_planner_any_layout_tile():
-    """Unaligned bf16: 128x128 tiles once their grid gives every CU two or
+    """Unaligned bf16: 128x128 tiles once their grid gives every CU one or
     more, else 64x64 tiles."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
-    # 4097 x 3001: 33 * 24 = 792 tiles of 128x128 (>= 512)
+    # 4097 x 3001: 33 * 24 = 792 tiles of 128x128 (>= 256)
     assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_any<128,128,32>"
     assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
     # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU
     p = plan(2047, 2047, 2047)
-    assert p["name"] == "mmrelu_bf16_any<64,64,32>" and p["grid"] == 32 * 32
-    assert plan(1001, 1001, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
-    # the threshold moves with the CU count: 2047^2 on 128 CUs takes 128x128
-    assert plan(2047, 2047, 2047, cus=128)["name"] == "mmrelu_bf16_any<128,128,32>"
-    # just at the threshold: 32 x 16 = 512 tiles
-    assert plan(4096, 2047, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
-    assert plan(4096 - 128, 2047, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
+    assert p["name"] == "mmrelu_bf16_any<128,128,32>" and p["grid"] == 16 * 16
+    p = plan(1001, 1001, 1001)
+    assert p["name"] == "mmrelu_bf16_any<64,64,32>" and p["grid"] == 16 * 16
+    # the threshold moves with the CU count: 1001^2 on 64 CUs takes 128x128
+    assert plan(1001, 1001, 1001, cus=64)["name"] == "mmrelu_bf16_any<128,128,32>"
+    # just at the threshold: 16 x 16 = 256 tiles, and one tile row fewer
+    assert plan(2048, 2047, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
+    assert plan(2048 - 128, 2047, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
 
 
 def test_every_variant_plans():

@@ -189,6 +189,60 @@ def test_guard_band_and_padded_leading_dimensions(dtype):
         assert np.all(np.isnan(wf[outside])), f"variant {v} wrote outside the window"
 
 
+def placed(x: np.ndarray, off: int, ld: int):
+    """A device buffer holding the compact matrix x with leading dimension ld,
+    starting `off` elements past a 16-byte boundary; NaN everywhere else (a
+    read outside x would poison the product). Returns (buffer, address)."""
+    rows, cols = x.shape
+    dt = torch.float32 if x.dtype == np.float32 else torch.bfloat16
+    flat = torch.full((off + rows * ld + 16,), float("nan"), dtype=dt, device="cuda")
+    flat[off:off + rows * ld].view(rows, ld)[:, :cols] = to_dev(x)
+    return flat, flat.data_ptr() + off * flat.element_size()
+
+
+# (dtype, element offsets of A, B, C, variants). Only element alignment is
+# required of pointers; these start A, B and C 1..7 elements past a 16-byte
+# boundary, through the planner (None) and the kernels that accept such
+# layouts: bf16 13/14 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
+# 11 (matrix-vector) and 0.
+MISALIGNED = [("bf16", (1, 3, 5), [None, 13, 14, 0]), ("bf16", (7, 2, 0), [None, 13, 14]),
+              ("bf16", (0, 0, 3), [None, 13]), ("f32", (1, 2, 3), [None, 2, 4, 0]), ("f32", (3, 0, 1), [None, 2, 4])]
+
+
+@pytest.mark.parametrize("dtype,offs,vs", MISALIGNED, ids=[f"{m[0]}-{m[1]}" for m in MISALIGNED])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (131, 97, 77)], ids=["even", "odd"])
+def test_element_aligned_pointers(dtype, offs, vs, M, N, K):
+    a = datagen.normal_f32(1700 + M, M, K, 1 / math.sqrt(K))
+    b = datagen.normal_f32(1800 + N, K, N, 1 / math.sqrt(K))
+    if dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a), datagen.f32_to_bf16_bits(b)
+    r = oracle.mmrelu(a, b)
+    lda, ldb, ldc = K + 5, N + 3, N + 1
+    fa, pa = placed(a, offs[0], lda)
+    fb, pb = placed(b, offs[1], ldb)
+    for v in vs:
+        print(f"misaligned {dtype} offs={offs} {M}x{N}x{K} variant={v}", flush=True)
+        fc, pc = placed(np.zeros((M, 0), a.dtype), offs[2], ldc)   # all NaN
+        args = (pa, pb, pc, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+        if dtype == "f32":
+            rc = mm.mmrelu_f32(*args) if v is None else mm.mmrelu_f32_variant(v, *args)
+        else:
+            rc = mm.mmrelu_bf16(*args) if v is None else mm.mmrelu_bf16_variant(v, *args)
+        assert rc == mm.MMRELU_OK, mm.status_string(rc)
+        torch.cuda.synchronize()
+        whole = to_host(fc)
+        c = whole[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+        if dtype == "f32":
+            check_f32(c[:, :N], r, K)
+            pad = c[:, N:].astype(np.float64)
+        else:
+            check_bf16(c[:, :N], r)
+            pad = datagen.bf16_bits_to_f32(c[:, N:]).astype(np.float64)
+        outside = np.concatenate([whole[:offs[2]], whole[offs[2] + M * ldc:]])
+        outside = outside.astype(np.float64) if dtype == "f32" else datagen.bf16_bits_to_f32(outside)
+        assert np.all(np.isnan(pad)) and np.all(np.isnan(outside)), f"variant {v} wrote outside C"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_k_zero_writes_zeros(dtype):
     M, N = 70, 136

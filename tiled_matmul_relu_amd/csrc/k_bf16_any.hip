@@ -1,21 +1,28 @@
 // bf16 act(A·B + bias) on the matrix cores for any layout: leading
 // dimensions, N and K need not be multiples of 8 nor rows 16-byte aligned,
-// which every other bf16 matrix-core kernel here requires. The lecture's
-// tiled recipe ("Kernels, Triton, XLA", section "Reductions and tiling") with
-// masked element loads:
+// which the DMA-fed bf16 kernels require. The lecture's tiled recipe
+// ("Kernels, Triton, XLA", section "Reductions and tiling"): one workgroup per
+// output tile, K swept in slabs staged in LDS, masked loads that read zeros
+// past the edges, fp32 accumulation, the activation on the accumulator, one
+// masked store.
 //  * BT x BT output tile (BT = 64 or 128) per workgroup of four waves
 //    (2 x 2), each wave a BT/2 x BT/2 sub-tile as blocks of
 //    v_mfma_f32_16x16x32_bf16; K in slabs of 32.
-//  * Each thread loads BT/8 elements of the A slab and as many of the B slab with
-//    bounds checks (zero outside M, N, K: the masked load with other = 0),
-//    one slab ahead in registers, and writes them to the other half of a
-//    double-buffered LDS. B is written transposed (column n holds its 32 k
-//    contiguously), so both operands' fragments (8 consecutive k of one row
-//    of A or one column of B) are single 16-byte LDS reads.
-//  * Epilogue as in the other kernels (bias, activation, one rounding to
-//    bf16), with a store per element so that any ldc works.
-// The element loads bound it well below the aligned kernels; it exists so
-// that no bf16 shape falls back to the plain (non-matrix-core) kernel.
+//  * Operands arrive in 16-byte pieces even when rows are misaligned: the 8
+//    elements a lane needs start e elements into an aligned 16-byte chunk,
+//    so the lane loads that chunk and the next and shifts the pair by e
+//    elements (v_alignbyte). Both loads are aligned and coalesced across the
+//    wave; elements past K (A) or past N (B) are then zeroed. Loads go
+//    through buffer resources whose range ends at the operand's last 16-byte
+//    granule: chunks past it read as zeros, and a 16-byte granule never
+//    crosses a page, so the bytes read around the operand are never
+//    unmapped.
+//  * A chunks land in LDS chunk-major per 16-row block and B rows row-major
+//    with XOR-swizzled chunks, the layouts of the aligned kernels, so
+//    fragments are one ds_read_b128 (A) and two ds_read_b64_tr_b16 (B).
+//  * One slab is loaded into registers while the previous one is
+//    multiplied; double-buffered LDS; bias, activation and one rounding to
+//    bf16 in the epilogue, with a store per element so any ldc works.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -26,53 +33,180 @@ namespace mmrelu {
 namespace {
 
 constexpr int kAnyBK = 32, kAnyThreads = 256;
-constexpr int kPitch = kAnyBK + 8;             // LDS row pitch in elements (80 bytes, 16-byte aligned)
 
 __device__ inline float bf16f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 
-// BT x BT output tile; four waves of (BT/2) x (BT/2), each NBLK x NBLK blocks.
+// XOR applied to the 16-byte chunk index of B row k in LDS (BT/8 chunks per
+// row): the 16 lanes of a transposed read touch rows k .. k+3 and spread
+// over the banks.
+template <int BT>
+__device__ inline int swz_row(int k)
+{
+    if constexpr (BT >= 128) return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+    else return (k & 3) << 1;
+}
+
+// (a & m) | (b & ~m): a per-lane select written as bit operations, so it
+// stays a v_bfi_b32 instead of becoming a branch.
+__device__ inline uint32_t pick(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// The 8 bf16 that start e elements (0 <= e < 8) into the 32 bytes lo:hi, in
+// three branch-free steps: shift by two dwords if e & 4, by one dword if
+// e & 2, then by half a dword if e & 1 (v_alignbyte).
+__device__ inline u32x4 realign(const u32x4 &lo, const u32x4 &hi, int e)
+{
+    const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint32_t m2 = 0u - ((static_cast<uint32_t>(e) >> 2) & 1u);
+    const uint32_t m1 = 0u - ((static_cast<uint32_t>(e) >> 1) & 1u);
+    const uint32_t sh = (static_cast<uint32_t>(e) & 1u) * 2u;
+    uint32_t x[6], y[5];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) x[j] = pick(m2, w[j + 2], w[j]);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) y[j] = pick(m1, x[j + 1], x[j]);
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __builtin_amdgcn_alignbyte(y[i + 1], y[i], sh);   // low dword of ({hi, lo} >> 8 sh)
+    return out;
+}
+
+// Keep the first v of the 8 bf16 in x (v <= 0: none), zero the rest.
+__device__ inline u32x4 keep_first(u32x4 x, int v)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (0u - static_cast<uint32_t>(2 * j < v)) & 0x0000FFFFu;
+        const uint32_t hi = (0u - static_cast<uint32_t>(2 * j + 1 < v)) & 0xFFFF0000u;
+        x[j] &= lo | hi;
+    }
+    return x;
+}
+
+// Resource over the bytes from base (any 2-byte aligned address) to
+// base + bytes, widened to whole 16-byte granules: the base is rounded down
+// and `mis` returns how many elements it moved.
+__device__ inline __amdgpu_buffer_rsrc_t granule_rsrc(const uint16_t *base, int64_t bytes, int &mis)
+{
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t al = p & ~static_cast<uintptr_t>(15);
+    mis = static_cast<int>((p - al) >> 1);
+    const int64_t n = bytes <= 0 ? 0 : ((bytes + static_cast<int64_t>(p - al) + 15) & ~int64_t{15});
+    return make_store_rsrc(reinterpret_cast<void *>(al), n);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 template <int BT>
 __global__ __launch_bounds__(kAnyThreads, 2) void mmrelu_bf16_any(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N, int K,
     int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m, const uint16_t *__restrict__ bias,
     int act)
 {
-    constexpr int kAnyBM = BT, kAnyBN = BT, NBLK = BT / 32;
-    constexpr int kPer = kAnyBM * kAnyBK / kAnyThreads;   // elements of A (and of B) per thread per slab
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kAnyBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Bt[2][kAnyBN * kPitch];
+    constexpr int NBLK = BT / 32;                         // 16x16 blocks per wave side
+    constexpr int kUnitsA = BT * (kAnyBK / 8);            // 16-byte chunks of an A slab
+    constexpr int kUnitsB = kAnyBK * (BT / 8);            // ... of a B slab
+    constexpr int kTA = kUnitsA / kAnyThreads, kTB = kUnitsB / kAnyThreads;
+    constexpr int kStage = (kUnitsA + kUnitsB) * 8;       // elements per stage
+    static_assert(kTA * kAnyThreads == kUnitsA && kTB * kAnyThreads == kUnitsB, "chunk split");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 4, t = lane & 15;
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * kAnyBM, n0 = tn * kAnyBN;
+    const int m0 = tm * BT, n0 = tn * BT;
 
-    // Slab loads: element e of this thread is A[m0 + r][k0 + k] with
-    // (r, k) = divmod(e * 256 + tid, 32), and B[k0 + k][n0 + n] with
-    // (k, n) = divmod(e * 256 + tid, BT): consecutive threads read
-    // consecutive columns of a row.
-    uint16_t ra[kPer], rb[kPer];
+    // A: chunk u (one per thread and pass) covers slab row u / 4, k 8q .. +7
+    // with q = u % 4 (four consecutive lanes read one row segment, which
+    // coalesces best). Its element offset from the rounded-down tile base is
+    // r lda + 8q + mis + k0, and k0 is a multiple of 8, so the shift e is
+    // fixed for the whole K loop and the slab only adds 2 k0 bytes.
+    int a_mis = 0;
+    const __amdgpu_buffer_rsrc_t ra =
+        granule_rsrc(A + static_cast<int64_t>(m0) * lda, (static_cast<int64_t>(M - 1 - m0) * lda + K) * 2, a_mis);
+    uint32_t a_vo[kTA];
+    int a_e[kTA];
+#pragma unroll
+    for (int x = 0; x < kTA; ++x) {
+        const int u = x * kAnyThreads + static_cast<int>(threadIdx.x);
+        const int r = u >> 2, q = u & 3;
+        const int64_t off = static_cast<int64_t>(r) * lda + 8 * q + a_mis;
+        a_e[x] = static_cast<int>(off & 7);
+        a_vo[x] = m0 + r < M ? static_cast<uint32_t>((off >> 3) * 16) : kOutOfRange;
+    }
+    // B: chunk u covers slab row u / (BT/8), columns 8 (u % (BT/8)) .. +7.
+    // The resource is rebased per slab (B + k0 ldb + n0), so the shifts are
+    // recomputed per slab.
+    u32x4 pa[kTA][2], pb[kTB][2];
+    int b_e[kTB];
+    // (The slab offset goes into the per-lane offset, not the scalar one, so
+    // that the resource's range check covers the whole address.)
     auto load = [&](int k0) __attribute__((always_inline)) {
+        const uint32_t kb = static_cast<uint32_t>(k0) * 2;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const int idx = e * kAnyThreads + static_cast<int>(threadIdx.x);
-            const int r = idx / kAnyBK, k = idx % kAnyBK;
-            const int gm = m0 + r, gk = k0 + k;
-            ra[e] = (gm < M && gk < K) ? A[static_cast<int64_t>(gm) * lda + gk] : uint16_t(0);
-            const int kb = idx / kAnyBN, n = idx % kAnyBN;
-            const int gkb = k0 + kb, gn = n0 + n;
-            rb[e] = (gkb < K && gn < N) ? B[static_cast<int64_t>(gkb) * ldb + gn] : uint16_t(0);
+        for (int x = 0; x < kTA; ++x) {
+            const bool ok = a_vo[x] != kOutOfRange;
+            pa[x][0] = load16(ra, ok ? a_vo[x] + kb : kOutOfRange, 0);
+            pa[x][1] = load16(ra, ok ? a_vo[x] + kb + 16 : kOutOfRange, 0);
+        }
+        int b_mis = 0;
+        const __amdgpu_buffer_rsrc_t rb = granule_rsrc(
+            B + static_cast<int64_t>(k0) * ldb + n0, (static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2, b_mis);
+#pragma unroll
+        for (int x = 0; x < kTB; ++x) {
+            const int u = x * kAnyThreads + static_cast<int>(threadIdx.x);
+            const int kr = u / (BT / 8), q = u % (BT / 8);
+            const int64_t off = static_cast<int64_t>(kr) * ldb + 8 * q + b_mis;
+            b_e[x] = static_cast<int>(off & 7);
+            const uint32_t vo = k0 + kr < K ? static_cast<uint32_t>((off >> 3) * 16) : kOutOfRange;
+            pb[x][0] = load16(rb, vo, 0);
+            pb[x][1] = load16(rb, vo == kOutOfRange ? kOutOfRange : vo + 16, 0);
         }
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
+    // Shift, mask and write the loaded slab into stage `buf`.
+    auto store = [&](int buf, int k0) __attribute__((always_inline)) {
+        uint16_t *st = lds + buf * kStage;
+        const bool k_tail = k0 + kAnyBK > K;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const int idx = e * kAnyThreads + static_cast<int>(threadIdx.x);
-            As[buf][(idx / kAnyBK) * kPitch + idx % kAnyBK] = ra[e];
-            Bt[buf][(idx % kAnyBN) * kPitch + idx / kAnyBN] = rb[e];   // transposed: column n, row k
+        for (int x = 0; x < kTA; ++x) {
+            const int u = x * kAnyThreads + static_cast<int>(threadIdx.x);
+            const int r = u >> 2, q = u & 3;
+            u32x4 v = realign(pa[x][0], pa[x][1], a_e[x]);
+            if (k_tail) v = keep_first(v, K - k0 - 8 * q);
+            *reinterpret_cast<u32x4 *>(st + ((((r >> 4) * 4 + q) * 16) + ((r & 15) ^ (4 * q))) * 8) = v;
+        }
+        const bool n_tail = n0 + BT > N;
+#pragma unroll
+        for (int x = 0; x < kTB; ++x) {
+            const int u = x * kAnyThreads + static_cast<int>(threadIdx.x);
+            const int kr = u / (BT / 8), q = u % (BT / 8);
+            u32x4 v = realign(pb[x][0], pb[x][1], b_e[x]);
+            if (n_tail) v = keep_first(v, N - n0 - 8 * q);
+            *reinterpret_cast<u32x4 *>(st + kUnitsA * 8 + kr * BT + ((q ^ swz_row<BT>(kr)) << 3)) = v;
         }
     };
+
+    // Fragment offsets (elements into a stage). A is chunk-major per 16-row
+    // block, as in the aligned kernels, with the row within the block XORed
+    // by 4q for chunk q: the 16 lanes that read one chunk still cover one
+    // contiguous 256-byte block, and the 16 lanes of a write (rows r .. r+3,
+    // chunks 0..3) land on 16 distinct units. A block i: rows
+    // wm*BT/2 + 16i + t, chunk g. B block j: lane t of group g reads row
+    // 8g + t/4 (+4 for the second half) at columns wn*BT/2 + 16j + 4(t%4) .. +3.
+    const int a_off = ((((wm * BT / 2) >> 4) * 4 + g) * 16 + (t ^ (4 * g))) * 8;
+    int b_off[NBLK];
+    {
+        const int k_lane = 8 * g + (t >> 2);
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) {
+            const int n = wn * (BT / 2) + j * 16 + 4 * (t & 3);
+            b_off[j] = kUnitsA * 8 + k_lane * BT + (((n >> 3) ^ swz_row<BT>(k_lane)) << 3) + (n & 7);
+        }
+    }
 
     f32x4 acc[NBLK][NBLK];
 #pragma unroll
@@ -81,25 +215,32 @@ __global__ __launch_bounds__(kAnyThreads, 2) void mmrelu_bf16_any(
         for (int j = 0; j < NBLK; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (K + kAnyBK - 1) / kAnyBK;
-    load(0);
-    store(0);
+    if (nk > 0) {
+        load(0);
+        store(0, 0);
+    }
     __syncthreads();
     for (int s = 0; s < nk; ++s) {
         const int buf = s & 1;
-        if (s + 1 < nk) load((s + 1) * kAnyBK);            // next slab in flight during the MFMAs
+        if (s + 1 < nk) load((s + 1) * kAnyBK);             // next slab in flight during the MFMAs
+        const uint16_t *st = lds + buf * kStage;
         bf16x8 fa[NBLK], fb[NBLK];
 #pragma unroll
-        for (int i = 0; i < NBLK; ++i)
-            fa[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * (BT / 2) + i * 16 + t) * kPitch + 8 * g]);
+        for (int i = 0; i < NBLK; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(st + a_off + i * 16 * kAnyBK);
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j)
-            fb[j] = *reinterpret_cast<const bf16x8 *>(&Bt[buf][(wn * (BT / 2) + j * 16 + t) * kPitch + 8 * g]);
+        for (int j = 0; j < NBLK; ++j) {
+            i16x4 half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(st + b_off[j] + 4 * h * BT));
+            fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
         for (int i = 0; i < NBLK; ++i)
 #pragma unroll
             for (int j = 0; j < NBLK; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        if (s + 1 < nk) store(buf ^ 1);                     // the other half: last read two slabs ago
+        if (s + 1 < nk) store(buf ^ 1, (s + 1) * kAnyBK);   // the other half: last read two slabs ago
         __syncthreads();
     }
 

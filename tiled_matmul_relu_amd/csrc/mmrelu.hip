@@ -139,12 +139,11 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     else if (fits) cand = bf16_aligned;
     else {
         // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 14)
-        // once their grid gives every CU two or more, else 64 x 64 tiles
-        // (variant 13); with one such workgroup per CU the larger tile runs
-        // slower than four smaller ones (measured: 2047^3, 104 against 95 us;
-        // 8191^2 x 1001, 0.51 against 0.64 ms).
+        // once their grid gives every CU one or more, else 64 x 64 tiles
+        // (variant 13), which keep more CUs busy (measured: 2047^3, 64.5
+        // against 76.7 us; 1001^3, 33.6 against 21.1 us).
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        return tiles128 >= 2 * static_cast<int64_t>(cus) ? 14 : 13;
+        return tiles128 >= static_cast<int64_t>(cus) ? 14 : 13;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
     // seven skinny tiles (variants 5 - 10 and 12), which split K over eight
