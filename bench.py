@@ -465,6 +465,7 @@ def main():
         for dtype in ("f32", "bf16"):
             shapes = [(n, n, n) for n in (256, 512, 1024, 2048, 4096, 8192)]
             shapes += [(m, 8192, 8192) for m in (1, 8, 16, 32, 64)] + [(8192, n, 8192) for n in (1, 16, 64)]
+            shapes += [(1, 16384, 16384), (4, 32768, 4096)]     # few rows, many columns
             # between skinny and square: few output tiles, long K; and the
             # ragged shape (odd leading dimensions)
             shapes += [(128, 8192, 8192), (256, 4096, 4096), (512, 512, 8192), (1024, 1024, 8192), (4097, 3001, 2049)]

@@ -22,6 +22,7 @@ import tiled_matmul_relu_amd as mm
 pytestmark = pytest.mark.gpu
 
 SKINNY = [5, 6, 7, 8, 9, 10, 12]  # tiles 16x32, 32x32, 64x32 (few rows), 32x16, 32x32, 32x64 (few columns), 64x64
+SKINNY_BF16 = SKINNY + [15]       # bf16 also: 16x64 strips (few rows, many columns)
 
 
 def to_dev(x: np.ndarray) -> torch.Tensor:
@@ -84,7 +85,7 @@ NK = [(32, 8), (264, 72), (1000, 1032), (520, 4096)]
 
 
 def run_all_skinny(dtype, a, b, M, N, K, r):
-    for v in SKINNY:
+    for v in (SKINNY_BF16 if dtype == "bf16" else SKINNY):
         print(f"{dtype} {M}x{N}x{K} variant={v}", flush=True)
         check(run(a, b, M, N, K, K, N, variant=v)[0], r, K, dtype)
 
@@ -161,7 +162,7 @@ def test_skinny_guard_band_padded(dtype, M, N):
     r = oracle.mmrelu(a, b, M=M, N=N, K=K, lda=lda, ldb=ldb)
     kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
     assert "skinny" in mm.mmrelu_plan(kind, M, N, K, lda, ldb, ldc)["name"]
-    for v in [None] + SKINNY:
+    for v in [None] + (SKINNY_BF16 if dtype == "bf16" else SKINNY):
         c, whole = run(a, b, M, N, K, lda, ldb, ldc=ldc, variant=v, guard=3)
         check(c, r, K, dtype)
         wf = whole.astype(np.float32) if dtype == "f32" else datagen.bf16_bits_to_f32(whole)

@@ -381,7 +381,14 @@ const Variant *variant_bf16_skinny(int mb, int nb, int ks)
                                launch_skinny<uint16_t, 2, 4, 2, 2>, 5.3f};
     static const Variant sq = {"mmrelu_skinny<bf16,64x64,ks2>", MMRELU_DTYPE_BF16, 64, 64, 64, kThreads, 1, 8,
                                launch_skinny<uint16_t, 4, 4, 2, 2>, 4.5f};
+    // 64-column strips for M <= 16 when N is large: whole 128-byte lines of B
+    // per row (measured: 1 x 16384 x 16384, 120.5 against 136.1 us on 32-column
+    // strips; 4 x 32768 x 4096, 44.5 against 49.5). At N = 8192 they leave
+    // half the CUs idle and tie with the 32-column strips.
+    static const Variant w1 = {"mmrelu_skinny<bf16,16x64,ks1>", MMRELU_DTYPE_BF16, 16, 64, 32, kThreads, 1, 8,
+                               launch_skinny<uint16_t, 1, 4, 1, 2>, 9.5f};
     if (nb == 4 && mb == 4) return &sq;
+    if (nb == 4 && mb == 1) return &w1;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;
     return nb == 1 ? &n1 : nb == 2 ? &n2 : &n4;
 }

@@ -16,7 +16,7 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 13;
-constexpr int kNumBf16 = 15;
+constexpr int kNumBf16 = 16;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -37,7 +37,7 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
-                                               variant_bf16_any(128)};
+                                               variant_bf16_any(128), variant_bf16_skinny(1, 4, 1)};
     return t;
 }
 
@@ -128,10 +128,13 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     // 32, 64 rows) or per 32 rows of A (skinny N: variants 8, 9, 10 for up to
     // 16, 32, 64 columns), with K split across eight waves. When both are
     // small, the smaller one decides.
+    // bf16 with at most 16 rows and a 64-column strip for every CU takes the
+    // 64-column strips (variant 15): whole 128-byte lines of B per row.
     if (fits && (M <= 64 || N <= 64)) {
         int32_t v;
         if (M <= 64 && M <= N) v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
         else v = N <= 16 ? 8 : N <= 32 ? 9 : 10;
+        if (v == 5 && dtype == MMRELU_DTYPE_BF16 && (N + 63) / 64 >= cus) v = 15;
         if (layout_fits(table[v], N, K, lda, ldb, ldc, A, B, C)) return v;
     }
     const int32_t *cand = nullptr;
