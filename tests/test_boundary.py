@@ -425,7 +425,10 @@ def test_planner_cost_model_uses_skinny_tiles_where_large_tiles_idle_cus():
         (B, 1024, 1024, 1024): "skinny<bf16,64x64,ks2>", (B, 4096, 128, 4096): "skinny<bf16,32x64,ks2>",
         (B, 128, 8192, 8192): "skinny<bf16,64x64,ks2>", (B, 256, 4096, 4096): "skinny<bf16,64x64,ks2>",
         (B, 256, 8192, 1024): "bf16_mfma<128,128", (B, 2048, 2048, 2048): "bf16_mfma<128,128",
-        (B, 4096, 4096, 4096): "pingpong", (B, 8192, 8192, 8192): "pingpong",
+        (B, 4096, 4096, 4096): "pingpong<256", (B, 8192, 8192, 8192): "pingpong<256",
+        # the 256 x 256 grid would fill half the CUs: 128 x 256 ping-pong tiles
+        (B, 1024, 8192, 8192): "pingpong<128,256", (B, 2048, 4096, 4096): "pingpong<128,256",
+        (B, 4096, 2048, 4096): "pingpong<128,256", (B, 3072, 3072, 3072): "pingpong<256",
     }
     for (dt, M, N, K), want in expect.items():
         name = plan(dt, M, N, K)["name"]

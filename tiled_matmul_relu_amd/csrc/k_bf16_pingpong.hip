@@ -59,26 +59,41 @@
 namespace mmrelu {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kBN = 256, kBK = 32;
 constexpr int kThreads = 512;
-constexpr int kMB = 8, kNB = 4;                       // MFMA blocks per wave: 128 x 64
+constexpr int kNB = 4;                                // MFMA column blocks per wave (64 columns)
 constexpr int kStagesA = 3, kStagesB = 4;
-constexpr int kStageABytes = kBM * 2 * kBK * 2;       // one pair of slabs of A: 32 KB
 constexpr int kStageBBytes = kBK * kBN * 2;           // one slab of B: 16 KB
-constexpr int kBBase = kStagesA * kStageABytes;       // byte offset of the B ring
-constexpr int kLdsBytes = kBBase + kStagesB * kStageBBytes;
-constexpr int kCopies = 4;                            // 1 KB copies per wave per memory interval
+constexpr int kCopiesB = 4;                           // 1 KB B copies per wave per memory interval
+
+// BM = 256 or 128 tile rows; each wave owns BM/2 x 64 outputs (kMB x 4 MFMA
+// blocks). The 128-row tile doubles the tile count for products whose
+// 256 x 256 grid leaves CUs idle.
+template <int BM>
+struct PingPong {
+    static_assert(BM == 256 || BM == 128, "tile rows");
+    static constexpr int kMB = BM / 32;
+    static constexpr int kStageABytes = BM * 2 * kBK * 2;    // one pair of slabs of A (BM x 64 k)
+    static constexpr int kBBase = kStagesA * kStageABytes;   // byte offset of the B ring
+    static constexpr int kLdsBytes = kBBase + kStagesB * kStageBBytes;
+    static constexpr int kCopiesA = BM / 64;                 // 1 KB A copies per wave per memory interval
+    static constexpr int kCopies = kCopiesA > kCopiesB ? kCopiesA : kCopiesB;
+};
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int ORDER>
+template <int BM, int ORDER>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
     const uint16_t *__restrict__ bias, int act)
 {
-    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsBytes / 2];
+    using P = PingPong<BM>;
+    constexpr int kMB = P::kMB, kStageABytes = P::kStageABytes, kBBase = P::kBBase, kCopies = P::kCopies;
+    constexpr int kHalf = BM / 2;                      // rows per half of an A pair, and per wave
+    static_assert(P::kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(ORDER != 4 || BM == 256, "the MFMA role issues two copies per column block");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[P::kLdsBytes / 2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,11 +103,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
 
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int m0 = tm * BM, n0 = tn * kBN;
     const uint32_t lds0 = lds_address(lds);
 
-    // Copy plans. Group 1, A: copy q of half hh of a pair covers rows
-    // 128hh + 8(4q + wl) .. +8; lane 8r'+j fetches chunk c = j ^ r' (8 k) of
+    // Copy plans. Group 1, A: copy q (q < BM/64) of half hh of a pair covers
+    // rows (BM/2)hh + 8(4q + wl) .. +8; lane 8r'+j fetches chunk c = j ^ r' (8 k) of
     // row r'. Rows past M get an out-of-range offset here, chunks past K per
     // pair. Group 0, B: copy q covers B rows 2(4q + wl) .. +2 of a slab,
     // lane l chunk (l%32) ^ swz(row); columns past N are masked here, rows
@@ -107,7 +122,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         if (grp == 1) {
             const int row = 8 * (4 * q + wl) + (lane >> 3);
             voff0[q] = (m0 + row < M) ? static_cast<uint32_t>((row * lda + 8 * a_chunk) * 2) : kOutOfRange;
-            voff1[q] = (m0 + 128 + row < M) ? static_cast<uint32_t>(((row + 128) * lda + 8 * a_chunk) * 2) : kOutOfRange;
+            voff1[q] = (m0 + kHalf + row < M) ? static_cast<uint32_t>(((row + kHalf) * lda + 8 * a_chunk) * 2)
+                                              : kOutOfRange;
         } else {
             const int row = 2 * (4 * q + wl) + (lane >> 5);
             const int col = ((lane & 31) ^ swz_b(row)) * 8;
@@ -115,11 +131,13 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
             voff1[q] = kOutOfRange;
         }
     }
-    // Copy q of half hh of A pair p (group 1).
+    // Copy q of half hh of A pair p (group 1); the 128-row tile has two
+    // copies per half (q >= 2 issues nothing).
     auto copy_a = [&](int p, int hh, int q) __attribute__((always_inline)) {
+        if (q >= P::kCopiesA) return;
         const int k0 = 2 * kBK * p;
         const uint32_t off = (8 * a_chunk < K - k0) ? (hh ? voff1[q] : voff0[q]) : kOutOfRange;
-        const uint32_t st = lds0 + (p % kStagesA) * kStageABytes + (128 * hh + 8 * (4 * q + wl)) * 128;
+        const uint32_t st = lds0 + (p % kStagesA) * kStageABytes + (kHalf * hh + 8 * (4 * q + wl)) * 128;
         load_to_lds<16>(ra, st, off, static_cast<uint32_t>(k0) * 2);
     };
     // Copy q of B slab m (group 0); rb is the B resource rebased to the slab.
@@ -133,10 +151,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     };
 
     // Fragment read plan (element offsets). A block i of slab s: rows
-    // wm*128 + 16i + t, chunk 4(s%2) + g of the pair. B block j: columns
+    // wm*BM/2 + 16i + t, chunk 4(s%2) + g of the pair. B block j: columns
     // wn*64 + 16j + 4(t%4), rows 8g + t/4 (+4h) of the slab.
-    const int a_off0 = (wm * 128 + t) * 64 + ((g ^ (t & 7)) << 3);
-    const int a_off1 = (wm * 128 + t) * 64 + (((4 + g) ^ (t & 7)) << 3);
+    const int a_off0 = (wm * kHalf + t) * 64 + ((g ^ (t & 7)) << 3);
+    const int a_off1 = (wm * kHalf + t) * 64 + (((4 + g) ^ (t & 7)) << 3);
     int b_off[kNB];
     {
         const int k_lane = 8 * g + (t >> 2);
@@ -148,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     }
 
     // Part p of the fragments of slab s: B block p (two transposed reads)
-    // and A blocks 2p, 2p+1.
+    // and A blocks p kMB/4 .. (p+1) kMB/4 - 1 (two, or one for 128 rows).
     bf16x8 fa[kMB], fb[kNB];
     auto read_part = [&](int s, int p) __attribute__((always_inline)) {
         const uint16_t *sa = lds + ((s >> 1) % kStagesA) * (kStageABytes / 2) + ((s & 1) ? a_off1 : a_off0);
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
             half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(sb + b_off[p] + 4 * h * kBN));
         fb[p] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int i = 2 * p; i < 2 * p + 2; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
+        for (int i = p * kMB / kNB; i < (p + 1) * kMB / kNB; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
     };
     // The memory role of one interval: read the fragments of slab `rd` (if
     // `do_read`) and issue this wave's four copies, copy(q). ORDER picks the
@@ -250,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                 for (int q = 0; q < kCopies; ++q) copy_b(m, q, rb);
             }
         }
-        interval_end(8);                             // slab 0 has landed
+        interval_end(grp == 1 ? 2 * P::kCopiesA : 2 * kCopiesB);   // slab 0 has landed
         if (grp == 0) {
             if constexpr (ORDER == 4) {
                 mem_work(0, true, no_copy);          // I_-1
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                 } else {
                     mfmas();                         // I_2k
                 }
-                interval_end(8);                     // slab k+1 has landed
+                interval_end(2 * kCopiesB);          // slab k+1 has landed
                 if constexpr (ORDER == 4) {          // I_2k+1
                     mem_work(k + 1, k + 1 < nk, no_copy);
                 } else {
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                     mfmas_copy([&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k+1
                 } else {
                     mem_work(k, true, [&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k
-                    interval_end(8);                 // slab k+1 has landed
+                    interval_end(2 * P::kCopiesA);   // slab k+1 has landed
                     mfmas();                         // I_2k+1
                 }
                 interval_end(-1);
@@ -317,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
         for (int i = 0; i < kMB; ++i) {
-            const int row = wm * 128 + i * 16 + t;
+            const int row = wm * kHalf + i * 16 + t;
 #pragma unroll
             for (int j = 0; j < kNB; ++j) {
                 const int col = wn * 64 + j * 16 + 4 * g;
@@ -333,11 +351,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     });
 }
 
-template <int ORDER, int GROUP_M>
+template <int BM, int ORDER, int GROUP_M>
 hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 {
-    const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((mmrelu_bf16_pingpong<ORDER>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + kBN - 1) / kBN;
+    hipLaunchKernelGGL((mmrelu_bf16_pingpong<BM, ORDER>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
                        static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M,
                        static_cast<const uint16_t *>(p.bias), p.act);
@@ -349,7 +367,17 @@ hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 const Variant *variant_bf16_pingpong256()
 {
     static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_pingpong<2, 8>};
+                              launch_pingpong<256, 2, 8>};
+    return &v;
+}
+// 128 x 256 tiles: twice the tiles of the 256 x 256 grid, for products that
+// would leave CUs idle on it. Relative cost per output 1.32 (8192^3: 1085
+// against 823 us); measured wins: 1024 x 8192 x 8192, 155 us against 175 on
+// 256 x 256 tiles and 179 on 128 x 128; 2048 x 4096 x 4096, 91 against 97.
+const Variant *variant_bf16_pingpong128()
+{
+    static const Variant v = {"mmrelu_bf16_pingpong<128,256,32,A3B4>", MMRELU_DTYPE_BF16, 128, 256, 32, 512, 1, 8,
+                              launch_pingpong<128, 2, 8>, 1.32f};
     return &v;
 }
 

@@ -16,7 +16,7 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 13;
-constexpr int kNumBf16 = 16;
+constexpr int kNumBf16 = 17;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -37,7 +37,8 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
-                                               variant_bf16_any(128), variant_bf16_skinny(1, 4, 1)};
+                                               variant_bf16_any(128), variant_bf16_skinny(1, 4, 1),
+                                               variant_bf16_pingpong128()};
     return t;
 }
 
@@ -171,6 +172,7 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     };
     consider(cand[0], true);
     consider(cand[1], true);
+    if (fits && dtype == MMRELU_DTYPE_BF16) consider(16, true);   // the 128 x 256 ping-pong tile
     if (fits) {
         for (int32_t v = 5; v <= 10; ++v) consider(v, false);
         consider(12, false);
