@@ -374,21 +374,32 @@ def row_stats(op, dtype, M, N, steps, warmup, torch, mm, datagen):
 
 
 def cpu_baseline(cfg, a, b, target_s, oracle):
-    """The oracle timed on rows [0, r) of the workload, r chosen from a short
-    calibration run so that the timed part takes about target_s seconds."""
+    """The oracle timed on rows [0, r) of the workload, r chosen so that the
+    timed part takes about target_s seconds: a calibration run on a few rows
+    per thread, one correction if the timed run came out under half the
+    target, and whole-matrix repeats if even all rows take under 10 s."""
     def run(rows):
         t0 = time.perf_counter()
         oracle.mmrelu(a, b, M=rows, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
         return time.perf_counter() - t0
-    cal_rows = 8
+    clamp = lambda r: int(min(cfg.M, max(1, r)))
+    cal_rows = clamp(max(64, 4 * oracle.num_threads()))
     t_cal = run(cal_rows)
-    rows = int(min(cfg.M, max(cal_rows, target_s / max(t_cal, 1e-6) * cal_rows)))
+    rows = clamp(target_s / max(t_cal, 1e-6) * cal_rows)
     t = run(rows)
-    flops = 2.0 * rows * cfg.N * cfg.K
+    if t < 0.5 * target_s and rows < cfg.M:
+        rows = clamp(rows * target_s / max(t, 1e-6))
+        t = run(rows)
+    reps = 1
+    if rows == cfg.M and t < 10.0:
+        reps = max(1, math.ceil(10.0 / max(t, 1e-6)))
+        t += sum(run(rows) for _ in range(reps - 1))
+    flops = 2.0 * rows * cfg.N * cfg.K * reps
+    what = f"rows 0..{rows - 1} of {cfg.M}" if rows < cfg.M else f"all {cfg.M} rows" + (f", {reps} times" if reps > 1 else "")
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of {cfg.M} of the {cfg.name} workload ({rows}x{cfg.N} outputs, "
-                      f"K={cfg.K}), fp64 oracle, {t:.1f} s"}
+            "sample": f"{what} of the {cfg.name} workload ({rows}x{cfg.N} outputs, K={cfg.K}), fp64 oracle, "
+                      f"{t:.1f} s"}
 
 
 def main():
