@@ -395,11 +395,12 @@ def cpu_baseline(cfg, a, b, target_s, oracle):
         reps = max(1, math.ceil(10.0 / max(t, 1e-6)))
         t += sum(run(rows) for _ in range(reps - 1))
     flops = 2.0 * rows * cfg.N * cfg.K * reps
-    what = f"rows 0..{rows - 1} of {cfg.M}" if rows < cfg.M else f"all {cfg.M} rows" + (f", {reps} times" if reps > 1 else "")
+    what = f"rows 0..{rows - 1} of {cfg.M}" if rows < cfg.M else f"all {cfg.M} rows"
+    times = f", computed {reps} times" if reps > 1 else ""
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{what} of the {cfg.name} workload ({rows}x{cfg.N} outputs, K={cfg.K}), fp64 oracle, "
-                      f"{t:.1f} s"}
+            "sample": f"{what} of the {cfg.name} workload ({rows}x{cfg.N} outputs, K={cfg.K}){times}, fp64 oracle, "
+                      f"{t:.1f} s in all"}
 
 
 def main():
