@@ -226,8 +226,8 @@ typedef struct {
  *   - an aligned layout with M <= 64 and M <= N: the skinny-M kernel of the
  *     smallest row count that covers M (16, 32 or 64 rows; it splits K over
  *     the eight waves of a workgroup so a 32-column strip of B streams from
- *     memory once); bf16 with M <= 16 and at least one 64-column strip per
- *     CU takes 64-column strips (variant 15);
+ *     memory once); M <= 16 with at least one 64-column strip per CU takes
+ *     64-column strips (fp32 variant 13, bf16 variant 15);
  *   - an aligned layout with N <= 64: the skinny-N kernel of the smallest
  *     column count that covers N (16, 32 or 64), over 32-row bands of A;
  *   - otherwise the candidate with the least estimated time on the busiest

@@ -100,12 +100,12 @@ def test_planner_picks_skinny_kernels_for_few_rows():
         for M, rows in ((1, 16), (16, 16), (17, 32), (32, 32), (33, 64), (64, 64)):
             p = mm.mmrelu_plan(dt, M, 8192, 8192, 8192, 8192, 8192, cus=256)
             assert "skinny" in p["name"] and p["block_m"] == rows and p["grid"] == 8192 // 32, (M, p["name"])
-        # bf16, at most 16 rows and one 64-column strip per CU or more: 16 x 64 strips
+        # at most 16 rows and one 64-column strip per CU or more: 16 x 64 strips
         p = mm.mmrelu_plan(dt, 4, 16384, 4096, 4096, 16384, 16384, cus=256)
-        if dt == mm.DTYPE_BF16:
-            assert (p["variant"], p["block_m"], p["block_n"], p["grid"]) == (15, 16, 64, 256), p
-        else:
-            assert (p["variant"], p["block_n"]) == (5, 32), p
+        want = 15 if dt == mm.DTYPE_BF16 else 13
+        assert (p["variant"], p["block_m"], p["block_n"], p["grid"]) == (want, 16, 64, 256), p
+        # ... but not at 8192 columns (128 strips of 64 for 256 CUs)
+        assert mm.mmrelu_plan(dt, 4, 8192, 4096, 4096, 8192, 8192, cus=256)["variant"] == 5
         assert mm.mmrelu_plan(dt, 17, 16384, 4096, 4096, 16384, 16384, cus=256)["variant"] == 6
         # past 64 rows the cost model decides, not the few-rows rule's 64 x 32
         # strips (fp32: 32 x 32 tiles, three row tiles; bf16: 64 x 64 tiles)

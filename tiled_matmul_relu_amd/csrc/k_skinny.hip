@@ -360,6 +360,13 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
                                launch_skinny<float, 2, 4, 2, 2>, 1.04f};
     static const Variant sq = {"mmrelu_skinny<float,64x64,ks2>", MMRELU_DTYPE_F32, 64, 64, 32, kThreads, 1, 4,
                                launch_skinny<float, 4, 4, 2, 2>, 1.03f};
+    // 64-column strips (256-byte rows of B) for M <= 16 when N is large:
+    // more 32-column strips than CUs read HBM more slowly (1 x 16384 x 8192:
+    // 4.8 TB/s, against 6.9 at 8192 columns); measured 1 x 16384 x 16384,
+    // 188.7 against 221.1 us; 16 x 16384 x 8192, 97.8 against 118.2.
+    static const Variant w1 = {"mmrelu_skinny<float,16x64,ks1>", MMRELU_DTYPE_F32, 16, 64, 16, kThreads, 1, 4,
+                               launch_skinny<float, 1, 4, 1, 2>, 2.3f};
+    if (nb == 4 && mb == 1) return &w1;
     if (nb == 4 && mb == 4) return &sq;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : &m2;
     if (nb == 2 && mb == 4) return &m4;

@@ -15,7 +15,7 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 13;
+constexpr int kNumF32 = 14;
 constexpr int kNumBf16 = 17;
 const Variant *const *f32_table()
 {
@@ -25,7 +25,7 @@ const Variant *const *f32_table()
                                               variant_f32_skinny(2, 2, 1), variant_f32_skinny(4, 2, 2),
                                               variant_f32_skinny(2, 1, 2), variant_f32_skinny(2, 2, 2),
                                               variant_f32_skinny(2, 4, 2), variant_f32_gemv(),
-                                              variant_f32_skinny(4, 4, 2)};
+                                              variant_f32_skinny(4, 4, 2), variant_f32_skinny(1, 4, 1)};
     return t;
 }
 const Variant *const *bf16_table()
@@ -129,13 +129,14 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     // 32, 64 rows) or per 32 rows of A (skinny N: variants 8, 9, 10 for up to
     // 16, 32, 64 columns), with K split across eight waves. When both are
     // small, the smaller one decides.
-    // bf16 with at most 16 rows and a 64-column strip for every CU takes the
-    // 64-column strips (variant 15): whole 128-byte lines of B per row.
+    // At most 16 rows and a 64-column strip for every CU: 64-column strips
+    // (fp32 variant 13, bf16 variant 15), which read whole lines of B per
+    // row (bf16) and keep the strip count at or under twice the CUs.
     if (fits && (M <= 64 || N <= 64)) {
         int32_t v;
         if (M <= 64 && M <= N) v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
         else v = N <= 16 ? 8 : N <= 32 ? 9 : 10;
-        if (v == 5 && dtype == MMRELU_DTYPE_BF16 && (N + 63) / 64 >= cus) v = 15;
+        if (v == 5 && (N + 63) / 64 >= cus) v = dtype == MMRELU_DTYPE_BF16 ? 15 : 13;
         if (layout_fits(table[v], N, K, lda, ldb, ldc, A, B, C)) return v;
     }
     const int32_t *cand = nullptr;
