@@ -230,6 +230,8 @@ typedef struct {
  *     64-column strips (fp32 variant 13, bf16 variant 15);
  *   - an aligned layout with N <= 64: the skinny-N kernel of the smallest
  *     column count that covers N (16, 32 or 64), over 32-row bands of A;
+ *     fp32 with N <= 16 and at least one 64-row band per CU takes 64-row
+ *     bands (variant 14);
  *   - otherwise the candidate with the least estimated time on the busiest
  *     compute unit, ceil(tiles / cus) tiles times the tile's outputs times
  *     the kernel's measured relative cost per output (times 1.15 for a tile

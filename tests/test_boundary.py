@@ -130,6 +130,13 @@ def test_planner_picks_skinny_kernels_for_few_columns():
         assert mm.mmrelu_plan(dt, 16, 64, 8192, 8192, 64, 64, cus=256)["block_m"] == 16
         p = mm.mmrelu_plan(dt, 64, 16, 8192, 8192, 16, 16, cus=256)
         assert (p["block_m"], p["block_n"]) == (32, 16)
+        # fp32, at most 16 columns and one 64-row band per CU or more: 64 x 16 bands
+        p = mm.mmrelu_plan(dt, 16384, 16, 8192, 8192, 16, 16, cus=256)
+        if dt == mm.DTYPE_F32:
+            assert (p["variant"], p["block_m"], p["block_n"], p["grid"]) == (14, 64, 16, 256), p
+        else:
+            assert (p["variant"], p["block_m"]) == (8, 32), p
+        assert mm.mmrelu_plan(dt, 16384, 24, 8192, 8192, 24, 24, cus=256)["variant"] == 9
 
 
 def test_skinny_variants_tile_any_shape():

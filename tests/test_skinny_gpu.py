@@ -22,7 +22,7 @@ import tiled_matmul_relu_amd as mm
 pytestmark = pytest.mark.gpu
 
 SKINNY = [5, 6, 7, 8, 9, 10, 12]  # tiles 16x32, 32x32, 64x32 (few rows), 32x16, 32x32, 32x64 (few columns), 64x64
-SKINNY_F32 = SKINNY + [13]        # fp32 also: 16x64 strips (few rows, many columns)
+SKINNY_F32 = SKINNY + [13, 14]    # fp32 also: 16x64 strips (few rows, many columns), 64x16 bands
 SKINNY_BF16 = SKINNY + [15]       # the same tile in the bf16 table
 
 

@@ -366,6 +366,12 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
     // 188.7 against 221.1 us; 16 x 16384 x 8192, 97.8 against 118.2.
     static const Variant w1 = {"mmrelu_skinny<float,16x64,ks1>", MMRELU_DTYPE_F32, 16, 64, 16, kThreads, 1, 4,
                                launch_skinny<float, 1, 4, 1, 2>, 2.3f};
+    // 64-row bands of A for N <= 16 when M is large, for the same reason
+    // (measured: 16384 x 16 x 8192, 122.6 against 150.4 us on 32-row bands;
+    // 32768 x 16 x 4096, 110.9 against 117.0). bf16 gains nothing from it.
+    static const Variant h1 = {"mmrelu_skinny<float,64x16,ks2>", MMRELU_DTYPE_F32, 64, 16, 32, kThreads, 1, 4,
+                               launch_skinny<float, 4, 1, 2, 2>, 2.3f};
+    if (nb == 1 && mb == 4) return &h1;
     if (nb == 4 && mb == 1) return &w1;
     if (nb == 4 && mb == 4) return &sq;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : &m2;

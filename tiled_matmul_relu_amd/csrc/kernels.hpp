@@ -52,8 +52,9 @@ const Variant *variant_bf16_mfma128();
 // the eight waves and ks k blocks per slab: (mb, nb, ks) = (1, 2, 1),
 // (2, 2, 1), (4, 2, 2 for fp32 / 1 for bf16) for skinny M, (2, 1, 2),
 // (2, 2, 2), (2, 4, 2) for skinny N, and (4, 4, 2), a 64 x 64 tile for
-// small squares and long-K products with few output tiles, and (1, 4, 1),
-// 16 x 64 strips for few rows and many columns.
+// small squares and long-K products with few output tiles, (1, 4, 1),
+// 16 x 64 strips for few rows and many columns, and (fp32) (4, 1, 2), 64 x 16
+// bands for few columns and many rows.
 const Variant *variant_f32_skinny(int mb, int nb, int ks);
 const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 // bf16 matrix-core kernel for any layout (k_bf16_any.hip).

@@ -15,7 +15,7 @@ namespace mmrelu {
 namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
-constexpr int kNumF32 = 14;
+constexpr int kNumF32 = 15;
 constexpr int kNumBf16 = 17;
 const Variant *const *f32_table()
 {
@@ -25,7 +25,8 @@ const Variant *const *f32_table()
                                               variant_f32_skinny(2, 2, 1), variant_f32_skinny(4, 2, 2),
                                               variant_f32_skinny(2, 1, 2), variant_f32_skinny(2, 2, 2),
                                               variant_f32_skinny(2, 4, 2), variant_f32_gemv(),
-                                              variant_f32_skinny(4, 4, 2), variant_f32_skinny(1, 4, 1)};
+                                              variant_f32_skinny(4, 4, 2), variant_f32_skinny(1, 4, 1),
+                                              variant_f32_skinny(4, 1, 2)};
     return t;
 }
 const Variant *const *bf16_table()
@@ -137,6 +138,9 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
         if (M <= 64 && M <= N) v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
         else v = N <= 16 ? 8 : N <= 32 ? 9 : 10;
         if (v == 5 && (N + 63) / 64 >= cus) v = dtype == MMRELU_DTYPE_BF16 ? 15 : 13;
+        // fp32, at most 16 columns and a 64-row band for every CU: 64-row
+        // bands (variant 14).
+        if (v == 8 && dtype == MMRELU_DTYPE_F32 && (M + 63) / 64 >= cus) v = 14;
         if (layout_fits(table[v], N, K, lda, ldb, ldc, A, B, C)) return v;
     }
     const int32_t *cand = nullptr;
