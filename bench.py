@@ -183,7 +183,49 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     ms = start.elapsed_time(end) / steps
     plan = mm.mmrelu_plan(mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16, cfg.M, cfg.N, cfg.K,
                           cfg.lda, cfg.ldb, cfg.ldc)
-    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b)}
+    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b), "da": da, "db": db}
+
+
+def mfma_ceiling(da, db, steps, warmup, torch):
+    """The bf16 matrix cores alone on the workload's own operand values
+    (probe/mfma_ceiling.hip): 1024 workgroups shaped like the 256 x 256 tiles
+    of the 8192^3 product, each wave issuing that product's MFMAs on operands
+    loaded once from A and B, no memory traffic in the loop. Timed like the
+    product (HIP events on the launch stream), for both MFMA shapes and for
+    all-zero operands. Returns TFLOP/s per case."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tiled_matmul_relu_amd", "_build",
+                        "libmfma_ceiling.so")
+    lib = ctypes.CDLL(path)
+    lib.mfma_ceiling_bf16.restype = ctypes.c_int
+    lib.mfma_ceiling_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    tiles, slabs = 1024, 256                      # 8192^3: (32 x 32) tiles of 256 x 256, 256 slabs of 32
+    flops = 2.0 * 256 * 256 * 32 * slabs * tiles
+    out = torch.empty(tiles * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    za, zb = torch.zeros_like(da), torch.zeros_like(db)
+    res = {}
+    for name, a, b in (("workload", da, db), ("zeros", za, zb)):
+        for shape in (16, 32):
+            def call():
+                rc = lib.mfma_ceiling_bf16(a.data_ptr(), b.data_ptr(), a.numel(), b.numel(), shape, tiles, slabs,
+                                           out.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mfma_ceiling_bf16 returned {rc}")
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for _ in range(steps):
+                call()
+            end.record(stream)
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(end) / steps
+            res[f"{name}_{shape}x{shape}"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    return res
 
 
 def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="relu", bias=False):
@@ -414,7 +456,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle timing")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32 4096^3 workload")
     ap.add_argument("--no-power-check", action="store_true",
-                    help="skip timing the bf16 kernel on all-zero inputs (the power-cap check)")
+                    help="skip the power-cap checks: the bf16 kernel on all-zero inputs, and the matrix cores alone "
+                         "on the workload's values (the MFMA ceiling probe)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a kernel of known traffic, "
                          "for scaling memory counters)")
@@ -596,6 +639,13 @@ def main():
         out["power_check"] = {"inputs": "all-zero bf16 A and B, same shape, kernel and launch",
                               "value": round(rz["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(rz["ms"], 4),
                               "frac": round(rz["tflops"] / PEAK_TFLOPS["bf16"], 4)}
+        # The matrix cores alone on the same operand values: the most any
+        # kernel of this product can reach on these inputs under the power cap.
+        mc = mfma_ceiling(res["da"], res["db"], args.steps, args.warmup, torch)
+        out["mfma_ceiling"] = {"what": "bf16 MFMAs alone (no memory traffic), the product's per-wave MFMA "
+                                       "block on operands loaded from A and B; TFLOP/s per MFMA shape",
+                               "unit": "TFLOP/s", **mc,
+                               "value_frac_of_ceiling": round(achieved / mc["workload_16x16"], 4)}
     if not args.no_f32:
         f = datagen.CONFIGS[3]
         r32 = time_workload(f, args.steps, args.warmup, torch, mm, datagen)

@@ -3,7 +3,9 @@
 Each ``csrc/*.hip`` file is compiled to an object in parallel, then linked
 into ``tiled_matmul_relu_amd/libmmrelu.so``. The C example
 (``examples/mmrelu_run.c``, the library used from C without Python) is then
-built with gcc against the library into ``_build/mmrelu_run``. Run ``python
+built with gcc against the library into ``_build/mmrelu_run``, and the
+matrix-core ceiling probe (``probe/mfma_ceiling.hip``, a measurement used by
+``bench.py --mfma-ceiling``) into ``_build/libmfma_ceiling.so``. Run ``python
 -m tiled_matmul_relu_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
@@ -21,6 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmmrelu.so")
 OBJDIR = os.path.join(PKG, "_build")
 EXAMPLE = os.path.join(OBJDIR, "mmrelu_run")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_ceiling.hip")
+PROBE_LIB = os.path.join(OBJDIR, "libmfma_ceiling.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -76,7 +80,19 @@ def build(jobs: int | None = None) -> str:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
     build_example()
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """The matrix-core ceiling probe (bench.py --mfma-ceiling), a library of
+    its own: it is a measurement, not part of libmmrelu."""
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), *HIPCC_FLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe build failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def build_example() -> str:
