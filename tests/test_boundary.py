@@ -187,7 +187,7 @@ def test_plans_for_the_workloads():
     assert p["tiles_m"] == -(-4097 // p["block_m"]) and p["tiles_n"] == -(-3001 // p["block_n"])
     # 8192^3 bf16: matrix-core kernel, whole waves
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 8192, 8192, 8192, 8192, 8192, 8192, cus=256)
-    assert "bf16_pingpong" in p["name"] and p["idle_slots_last"] == 0
+    assert p["name"] == "mmrelu_bf16_pingpong<256,256,64,A3B4>" and p["idle_slots_last"] == 0
     # bf16 with N, K or a leading dimension off the 8-element grid: the
     # any-layout matrix-core kernel
     p = mm.mmrelu_plan(mm.DTYPE_BF16, 100, 100, 100, 100, 100, 100, cus=256)
@@ -432,10 +432,10 @@ def test_planner_cost_model_uses_skinny_tiles_where_large_tiles_idle_cus():
         (B, 1024, 1024, 1024): "skinny<bf16,64x64,ks2>", (B, 4096, 128, 4096): "skinny<bf16,32x64,ks2>",
         (B, 128, 8192, 8192): "skinny<bf16,64x64,ks2>", (B, 256, 4096, 4096): "skinny<bf16,64x64,ks2>",
         (B, 256, 8192, 1024): "bf16_mfma<128,128", (B, 2048, 2048, 2048): "bf16_mfma<128,128",
-        (B, 4096, 4096, 4096): "pingpong<256", (B, 8192, 8192, 8192): "pingpong<256",
+        (B, 4096, 4096, 4096): "pingpong<256,256,64", (B, 8192, 8192, 8192): "pingpong<256,256,64",
         # the 256 x 256 grid would fill half the CUs: 128 x 256 ping-pong tiles
-        (B, 1024, 8192, 8192): "pingpong<128,256", (B, 2048, 4096, 4096): "pingpong<128,256",
-        (B, 4096, 2048, 4096): "pingpong<128,256", (B, 3072, 3072, 3072): "pingpong<256",
+        (B, 1024, 8192, 8192): "pingpong<128,256,64", (B, 2048, 4096, 4096): "pingpong<128,256,64",
+        (B, 4096, 2048, 4096): "pingpong<128,256,64", (B, 3072, 3072, 3072): "pingpong<256,256,64",
     }
     for (dt, M, N, K), want in expect.items():
         name = plan(dt, M, N, K)["name"]

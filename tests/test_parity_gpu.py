@@ -106,6 +106,8 @@ F32_SHAPES = [  # (M, N, K) spanning several tiles with ragged tails, plus degen
 BF16_SHAPES = [
     (8, 8, 8), (1, 8, 8), (264, 520, 136), (256, 256, 64), (300, 264, 72), (520, 8, 200),
     (16, 512, 1032), (3, 5, 7), (257, 131, 67),
+    # K mod 64 = 24 and 40: the last 64-deep pair of slabs is partly past K
+    (136, 512, 88), (264, 256, 104), (256, 512, 1000),
 ]
 
 

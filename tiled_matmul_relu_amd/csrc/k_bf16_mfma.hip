@@ -347,10 +347,12 @@ const Variant *variant_bf16_mfma256_8w()
 
 // 128 x 128 tiles (2 x 2 waves of 64 x 64): four times the workgroups of the
 // 256 x 256 tile, for shapes whose 256 x 256 grid leaves most CUs idle.
+// Relative cost per output 1.66 against the 64-deep 256 x 256 ping-pong tile
+// (1.55 against the 32-deep one, times its speedup 1.067).
 const Variant *variant_bf16_mfma128()
 {
     static const Variant v = {"mmrelu_bf16_mfma<128,128,32,4,2,2,prefetch>", MMRELU_DTYPE_BF16, 128, 128, 32, 256, 2, 8,
-                              launch_bf16<128, 128, 32, 4, 2, 2, true, 8>, 1.55f};
+                              launch_bf16<128, 128, 32, 4, 2, 2, true, 8>, 1.66f};
     return &v;
 }
 

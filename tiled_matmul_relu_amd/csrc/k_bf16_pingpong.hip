@@ -48,6 +48,25 @@
 // read), so every interval costs the same vmcnt count and the loop has no
 // data-dependent branches.
 //
+// Deep intervals (DEPTH = 2): each interval covers a PAIR of slabs, 64 k.
+// The MFMA role issues 64 MFMAs per interval instead of 32, and the memory
+// role reads both slabs' fragments (two register sets) and issues the
+// pair's copies. The LDS layout and rings are the same. A memory interval's
+// fragment reads take longer than 32 MFMAs (about 640 cycles against 512,
+// measured on a register-and-LDS probe), so the 32-deep schedule leaves
+// the matrix cores idle at every barrier; 64 MFMAs cover the reads, and the
+// barriers halve. Schedule (J_t ends at a barrier; pair p = slabs 2p, 2p+1):
+//   prologue: group 1 copies A pairs 0 and 1, group 0 B pair 0; wait for
+//             pair 0; barrier. J_-1: group 0 reads pair 0, copies B pair 1.
+//   J_2p:   group 0 multiplies pair p, then waits for all its copies (B
+//           pair p+1, issued in J_2p-1);
+//           group 1 reads pair p, copies A pair p+2, then waits for all but
+//           those (A pair p+1, issued in J_2p-2).
+//   J_2p+1: group 0 reads pair p+1 and copies B pair p+2 (into the stages
+//           of pair p, which group 1 read in J_2p);
+//           group 1 multiplies pair p.
+// A pair p+2's stage last held pair p-1, read by group 1 in J_2p-2.
+//
 // Requires lda, ldb, ldc, K and N to be multiples of 8 and 16-byte aligned
 // pointers.
 #include <type_traits>
@@ -82,7 +101,7 @@ struct PingPong {
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int BM, int ORDER>
+template <int BM, int ORDER, int DEPTH>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
@@ -93,6 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     constexpr int kHalf = BM / 2;                      // rows per half of an A pair, and per wave
     static_assert(P::kLdsBytes <= 160 * 1024, "LDS budget");
     static_assert(ORDER != 4 || BM == 256, "the MFMA role issues two copies per column block");
+    static_assert(DEPTH == 1 || (DEPTH == 2 && ORDER == 2), "slabs per interval; deep intervals pair copies and reads");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[P::kLdsBytes / 2];
 
     const int lane = threadIdx.x & 63;
@@ -165,19 +185,21 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         }
     }
 
-    // Part p of the fragments of slab s: B block p (two transposed reads)
-    // and A blocks p kMB/4 .. (p+1) kMB/4 - 1 (two, or one for 128 rows).
-    bf16x8 fa[kMB], fb[kNB];
-    auto read_part = [&](int s, int p) __attribute__((always_inline)) {
+    // Part p of the fragments of slab s, into register set d: B block p (two
+    // transposed reads) and A blocks p kMB/4 .. (p+1) kMB/4 - 1 (two, or one
+    // for 128 rows). Deep intervals hold a pair of slabs in sets 0 and 1.
+    bf16x8 fa[DEPTH][kMB], fb[DEPTH][kNB];
+    auto read_part = [&](int s, int p, int d) __attribute__((always_inline)) {
         const uint16_t *sa = lds + ((s >> 1) % kStagesA) * (kStageABytes / 2) + ((s & 1) ? a_off1 : a_off0);
         const uint16_t *sb = lds + (s % kStagesB) * (kStageBBytes / 2);
         i16x4 half[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(sb + b_off[p] + 4 * h * kBN));
-        fb[p] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        fb[d][p] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int i = p * kMB / kNB; i < (p + 1) * kMB / kNB; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
+        for (int i = p * kMB / kNB; i < (p + 1) * kMB / kNB; ++i)
+            fa[d][i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
     };
     // The memory role of one interval: read the fragments of slab `rd` (if
     // `do_read`) and issue this wave's four copies, copy(q). ORDER picks the
@@ -189,24 +211,33 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
             (void)copy;
             if (do_read)
 #pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
         } else if constexpr (ORDER == 0 || ORDER == 1) {
             if (ORDER == 0 && do_read)
 #pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
 #pragma unroll
             for (int q = 0; q < kCopies; ++q) copy(q);
             if (ORDER == 1 && do_read)
 #pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p);
+                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
         } else {
             static_assert(kNB == kCopies, "one copy per fragment part");
 #pragma unroll
             for (int p = 0; p < kNB; ++p) {
                 if (ORDER == 2) copy(p);
-                if (do_read) read_part(rd, p);
+                if (do_read) read_part(rd, p, 0);
                 if (ORDER == 3) copy(p);
             }
+        }
+    };
+    // The memory role of a deep interval: read both slabs of pair pp (if
+    // `do_read`) and issue this wave's eight copies, copy(q) before part q.
+    auto mem_work_pair = [&](int pp, bool do_read, auto &&copy) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 2 * kNB; ++q) {
+            copy(q);
+            if (do_read) read_part(2 * pp + q / kNB, q % kNB, q / kNB);
         }
     };
 
@@ -217,10 +248,12 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto mfmas = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+        for (int d = 0; d < DEPTH; ++d)
 #pragma unroll
-            for (int j = 0; j < kNB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[d][j], fa[d][i], acc[i][j], 0, 0, 0);
     };
     // ORDER 4: the MFMA role issues the copies, one after every 8 MFMAs.
     auto mfmas_copy = [&](auto &&copy) __attribute__((always_inline)) {
@@ -228,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         for (int i = 0; i < kMB; ++i) {
 #pragma unroll
             for (int j = 0; j < kNB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
             if (i & 1) {
                 __builtin_amdgcn_sched_barrier(0);
                 copy(i >> 1);
@@ -245,6 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         __builtin_amdgcn_sched_barrier(0);
         if (in_flight == 8) wait_vmcnt<8>();
         if (in_flight == 4) wait_vmcnt<4>();
+        if (in_flight == 0) wait_vmcnt<0>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -252,7 +286,56 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     // Each group runs its own loop (one copy of the fragment registers and
     // the MFMA chain per code path); both execute the same barriers.
     const int nk = (K + kBK - 1) / kBK;
-    if (nk > 0) {
+    if constexpr (DEPTH == 2) {
+        const int np = (K + 2 * kBK - 1) / (2 * kBK);
+        // Copy q (< 8) of A pair p (group 1): half q / kCopiesA; the 128-row
+        // tile has four copies per pair (q >= 4 issues nothing).
+        auto copy_a_pair = [&](int p, int q) __attribute__((always_inline)) {
+            if (q < 2 * P::kCopiesA) copy_a(p, q / P::kCopiesA, q % P::kCopiesA);
+        };
+        if (np > 0) {
+            if (grp == 1) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int q = 0; q < 2 * kNB; ++q) copy_a_pair(p, q);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const rsrc_t rb = b_rsrc(m);
+#pragma unroll
+                    for (int q = 0; q < kCopiesB; ++q) copy_b(m, q, rb);
+                }
+            }
+            interval_end(grp == 1 ? 2 * P::kCopiesA : 0);   // pair 0 has landed
+            if (grp == 0) {
+                {
+                    const rsrc_t rb0 = b_rsrc(2), rb1 = b_rsrc(3);
+                    mem_work_pair(0, true, [&](int q) __attribute__((always_inline)) {
+                        copy_b(2 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
+                    });                                               // J_-1
+                }
+                interval_end(-1);
+                for (int p = 0; p < np; ++p) {
+                    mfmas();                                          // J_2p
+                    interval_end(0);                                  // B pair p+1 has landed
+                    const rsrc_t rb0 = b_rsrc(2 * p + 4), rb1 = b_rsrc(2 * p + 5);
+                    mem_work_pair(p + 1, p + 1 < np, [&](int q) __attribute__((always_inline)) {
+                        copy_b(2 * p + 4 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
+                    });                                               // J_2p+1
+                    interval_end(-1);
+                }
+            } else {
+                interval_end(-1);                                     // J_-1
+                for (int p = 0; p < np; ++p) {
+                    mem_work_pair(p, true, [&](int q) __attribute__((always_inline)) { copy_a_pair(p + 2, q); });
+                    interval_end(2 * P::kCopiesA);                    // A pair p+1 has landed
+                    mfmas();                                          // J_2p+1
+                    interval_end(-1);
+                }
+            }
+        }
+    } else if (nk > 0) {
         if (grp == 1) {
 #pragma unroll
             for (int p = 0; p < 2; ++p)
@@ -351,11 +434,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     });
 }
 
-template <int BM, int ORDER, int GROUP_M>
+template <int BM, int ORDER, int GROUP_M, int DEPTH>
 hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((mmrelu_bf16_pingpong<BM, ORDER>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((mmrelu_bf16_pingpong<BM, ORDER, DEPTH>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
                        static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M,
                        static_cast<const uint16_t *>(p.bias), p.act);
@@ -367,7 +450,7 @@ hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 const Variant *variant_bf16_pingpong256()
 {
     static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_pingpong<256, 2, 8>};
+                              launch_pingpong<256, 2, 8, 1>};
     return &v;
 }
 // 128 x 256 tiles: twice the tiles of the 256 x 256 grid, for products that
@@ -377,7 +460,27 @@ const Variant *variant_bf16_pingpong256()
 const Variant *variant_bf16_pingpong128()
 {
     static const Variant v = {"mmrelu_bf16_pingpong<128,256,32,A3B4>", MMRELU_DTYPE_BF16, 128, 256, 32, 512, 1, 8,
-                              launch_pingpong<128, 2, 8>, 1.32f};
+                              launch_pingpong<128, 2, 8, 1>, 1.32f};
+    return &v;
+}
+
+// Deep intervals (64 k per interval, one barrier per 64 k) on the same tiles:
+// the planner's bf16 tile kernels. Measured against the 32-deep schedule on
+// one box: 8192^3, 753 against 804 us (N(0,1)/sqrt(K) inputs) and 578
+// against 630 (zeros); 4096^3, 104 against 110; 1024 x 8192 x 8192 on the
+// 128-row tile, 126 against 137.
+const Variant *variant_bf16_pingpong256_deep()
+{
+    static const Variant v = {"mmrelu_bf16_pingpong<256,256,64,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 64, 512, 1, 8,
+                              launch_pingpong<256, 2, 8, 2>};
+    return &v;
+}
+// Relative cost per output 1.33: one 128 x 256 tile of K = 8192 per CU takes
+// 126 us (1024 x 8192 x 8192), a 256 x 256 tile 188 us (a quarter of 8192^3).
+const Variant *variant_bf16_pingpong128_deep()
+{
+    static const Variant v = {"mmrelu_bf16_pingpong<128,256,64,A3B4>", MMRELU_DTYPE_BF16, 128, 256, 64, 512, 1, 8,
+                              launch_pingpong<128, 2, 8, 2>, 1.33f};
     return &v;
 }
 

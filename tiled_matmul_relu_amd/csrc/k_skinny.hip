@@ -328,7 +328,7 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 
 // Skinny-M tiles (16, 32 or 64 rows by 32 columns), skinny-N tiles (32
 // rows by 16, 32 or 64 columns) and the 64 x 64 tile (relative cost 1.03
-// fp32, 4.5 bf16: measured 1024^3 fp32 25.7 against 27.5 us on 32 x 64
+// fp32, 4.8 bf16: measured 1024^3 fp32 25.7 against 27.5 us on 32 x 64
 // tiles, bf16 10.0 against 12.7; 1024 x 1024 x 8192 bf16 48.6 against 65).
 // Any shape is covered by a grid of tiles;
 // the planner uses them where one dimension is small, and through its cost
@@ -336,7 +336,9 @@ hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 // output (against the dtype's fastest tile kernel at full occupancy) was
 // fitted on 256^3 .. 2048^3, 512 x 512 x 8192, 1024 x 1024 x 8192 and
 // 128 / 4096-row products: about 1.04 - 1.1 in fp32, 5.3 - 9.5 in bf16 (the
-// bf16 ping-pong kernel does far more per output at full occupancy); the
+// bf16 ping-pong kernel does far more per output at full occupancy), the
+// bf16 figures then scaled by 1.067 when the 64-deep ping-pong schedule
+// became the reference (8192^3: 753 against 804 us); the
 // 16-wide tiles, slower per output, are priced up so that the planner uses
 // them only through the few-rows and few-columns rules. Each uses the k depth
 // per slab (KS) and ring depth measured fastest for its role at 8192 x 8192:
@@ -381,25 +383,25 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
 const Variant *variant_bf16_skinny(int mb, int nb, int ks)
 {
     static const Variant m1 = {"mmrelu_skinny<bf16,16x32,ks1>", MMRELU_DTYPE_BF16, 16, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 1, 2, 1, 2>, 9.5f};
+                               launch_skinny<uint16_t, 1, 2, 1, 2>, 10.1f};
     static const Variant m2 = {"mmrelu_skinny<bf16,32x32,ks1>", MMRELU_DTYPE_BF16, 32, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 2, 1, 2>, 9.5f};
+                               launch_skinny<uint16_t, 2, 2, 1, 2>, 10.1f};
     static const Variant m4 = {"mmrelu_skinny<bf16,64x32,ks1>", MMRELU_DTYPE_BF16, 64, 32, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 4, 2, 1, 2>, 6.0f};
+                               launch_skinny<uint16_t, 4, 2, 1, 2>, 6.4f};
     static const Variant n1 = {"mmrelu_skinny<bf16,32x16,ks2>", MMRELU_DTYPE_BF16, 32, 16, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 1, 2, 2>, 9.5f};
+                               launch_skinny<uint16_t, 2, 1, 2, 2>, 10.1f};
     static const Variant n2 = {"mmrelu_skinny<bf16,32x32,ks2>", MMRELU_DTYPE_BF16, 32, 32, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 2, 2, 2>, 9.0f};
+                               launch_skinny<uint16_t, 2, 2, 2, 2>, 9.6f};
     static const Variant n4 = {"mmrelu_skinny<bf16,32x64,ks2>", MMRELU_DTYPE_BF16, 32, 64, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 2, 4, 2, 2>, 5.3f};
+                               launch_skinny<uint16_t, 2, 4, 2, 2>, 5.7f};
     static const Variant sq = {"mmrelu_skinny<bf16,64x64,ks2>", MMRELU_DTYPE_BF16, 64, 64, 64, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 4, 4, 2, 2>, 4.5f};
+                               launch_skinny<uint16_t, 4, 4, 2, 2>, 4.8f};
     // 64-column strips for M <= 16 when N is large: whole 128-byte lines of B
     // per row (measured: 1 x 16384 x 16384, 120.5 against 136.1 us on 32-column
     // strips; 4 x 32768 x 4096, 44.5 against 49.5). At N = 8192 they leave
     // half the CUs idle and tie with the 32-column strips.
     static const Variant w1 = {"mmrelu_skinny<bf16,16x64,ks1>", MMRELU_DTYPE_BF16, 16, 64, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 1, 4, 1, 2>, 9.5f};
+                               launch_skinny<uint16_t, 1, 4, 1, 2>, 10.1f};
     if (nb == 4 && mb == 4) return &sq;
     if (nb == 4 && mb == 1) return &w1;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;

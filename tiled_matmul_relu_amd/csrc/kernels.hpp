@@ -47,6 +47,8 @@ const Variant *variant_bf16_mfma256();
 const Variant *variant_bf16_mfma256_8w();
 const Variant *variant_bf16_pingpong256();
 const Variant *variant_bf16_pingpong128();
+const Variant *variant_bf16_pingpong256_deep();
+const Variant *variant_bf16_pingpong128_deep();
 const Variant *variant_bf16_mfma128();
 // Skinny kernels (k_skinny.hip), tiles of 16 mb x 16 nb with K split over
 // the eight waves and ks k blocks per slab: (mb, nb, ks) = (1, 2, 1),

@@ -16,7 +16,7 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 15;
-constexpr int kNumBf16 = 17;
+constexpr int kNumBf16 = 19;
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -39,7 +39,8 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
                                                variant_bf16_any(128), variant_bf16_skinny(1, 4, 1),
-                                               variant_bf16_pingpong128()};
+                                               variant_bf16_pingpong128(), variant_bf16_pingpong256_deep(),
+                                               variant_bf16_pingpong128_deep()};
     return t;
 }
 
@@ -118,7 +119,7 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                        const void *A, const void *B, const void *C, int32_t cus)
 {
-    static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {3, 4};
+    static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {17, 4};
     const Variant *const *table = dtype == MMRELU_DTYPE_F32 ? f32_table() : bf16_table();
     // A single output column is a matrix-vector product: one read of A, one
     // wave per output (variant 11), whatever the layout.
@@ -177,7 +178,7 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     };
     consider(cand[0], true);
     consider(cand[1], true);
-    if (fits && dtype == MMRELU_DTYPE_BF16) consider(16, true);   // the 128 x 256 ping-pong tile
+    if (fits && dtype == MMRELU_DTYPE_BF16) consider(18, true);   // the 128 x 256 ping-pong tile
     if (fits) {
         for (int32_t v = 5; v <= 10; ++v) consider(v, false);
         consider(12, false);
