@@ -320,9 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                     mfmas();                                          // J_2p
                     interval_end(0);                                  // B pair p+1 has landed
                     const rsrc_t rb0 = b_rsrc(2 * p + 4), rb1 = b_rsrc(2 * p + 5);
-                    mem_work_pair(p + 1, p + 1 < np, [&](int q) __attribute__((always_inline)) {
+                    auto copy_b_pair = [&](int q) __attribute__((always_inline)) {
                         copy_b(2 * p + 4 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
-                    });                                               // J_2p+1
+                    };
+                    // J_2p+1. The last pair has nothing left to read; one
+                    // branch here, not one per fragment part (1.5% faster at
+                    // 8192^3).
+                    if (p + 1 < np) mem_work_pair(p + 1, true, copy_b_pair);
+                    else mem_work_pair(p + 1, false, copy_b_pair);
                     interval_end(-1);
                 }
             } else {
