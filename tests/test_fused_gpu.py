@@ -106,7 +106,8 @@ def inputs(dtype, M, N, K, seed, scale=None):
 
 
 SHAPES = {"f32": [(257, 131, 67), (264, 520, 136), (70, 64, 200)],
-          "bf16": [(264, 520, 136), (300, 264, 72), (257, 131, 67)]}
+          # K = 104: the last 64-deep pair of the ping-pong kernel is partly past K
+          "bf16": [(264, 520, 136), (300, 264, 72), (257, 131, 67), (136, 264, 104)]}
 
 
 @pytest.mark.parametrize("act", sorted(ACTS))
