@@ -255,6 +255,29 @@ def test_k_zero_writes_zeros(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_k_zero_every_variant_writes_zeros(dtype):
+    """K = 0: the loop over K runs zero times and every kernel stores
+    relu(0) = 0 over a C filled with NaN beforehand (the empty sum)."""
+    M, N = 264, 520
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    # A is M x 1 and B 1 x N (lda = 1, ldb = N), as the operands of a K = 1
+    # product: any range a kernel derives from M, N and the leading
+    # dimensions stays inside them.
+    a = torch.zeros((M, 1), dtype=tdt, device="cuda")
+    b = torch.zeros((1, N), dtype=tdt, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for v in variants(kind):
+        c = torch.full((M, N), float("nan"), dtype=tdt, device="cuda")
+        fn = mm.mmrelu_f32_variant if dtype == "f32" else mm.mmrelu_bf16_variant
+        print(f"k=0 {dtype} variant={v}", flush=True)
+        rc = fn(v, a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, 0, 1, N, N, s)
+        assert rc == mm.MMRELU_OK, (v, mm.status_string(rc))
+        torch.cuda.synchronize()
+        assert bool((c == 0).all()), f"variant {v}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_zero_inputs_give_zero_outputs(dtype):
     """All-zero A and B (the inputs of bench.py's power check): every variant
     writes +0 or -0 everywhere, over several tiles and a ragged tail."""
