@@ -237,8 +237,10 @@ typedef struct {
  *     the kernel's measured relative cost per output (times 1.15 for a tile
  *     kernel left with one tile per CU, which then runs latency-bound).
  *     Candidates: the dtype's matrix-core kernels at a large and a small
- *     tile that accept the layout (for aligned bf16 also the 128 x 256
- *     ping-pong tile, variant 16) and, for aligned layouts, the seven
+ *     tile that accept the layout (aligned bf16: the 256 x 256 ping-pong
+ *     tile with 64-deep intervals, variant 17, the 128 x 128 tile, variant
+ *     4, and the 128 x 256 ping-pong tile, variant 18) and, for aligned
+ *     layouts, the seven
  *     skinny tiles (variants 5 - 10 and the 64 x 64 variant 12), which split
  *     K over eight waves and keep every CU busy when the large tiles cannot
  *     (small squares, long K with few output tiles); other layouts run the
