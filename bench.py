@@ -160,10 +160,15 @@ def to_device(x, torch):
 
 
 def time_workload(cfg, steps, warmup, torch, mm, datagen):
+    """W warm-up calls, then `steps` calls back to back between two HIP events
+    on the launch stream (the timed region: ms per call = elapsed / steps),
+    then `steps` more calls with an event after each, for the distribution
+    of single calls (mean, median, P95). Returns the times, the plan, the
+    host inputs and the device output of the last call."""
     a, b = datagen.make_inputs(cfg)
     da, db = to_device(a, torch), to_device(b, torch)
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
-    c = torch.empty((cfg.M, cfg.ldc), dtype=dt, device="cuda")
+    c = torch.full((cfg.M, cfg.ldc), float("nan"), dtype=dt, device="cuda")
     stream = torch.cuda.current_stream()
     fn = mm.mmrelu_f32 if cfg.dtype == "f32" else mm.mmrelu_bf16
     args = (da.data_ptr(), db.data_ptr(), c.data_ptr(), cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc,
@@ -181,9 +186,25 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(*args)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    per_call = {"calls": steps, "mean_ms": round(sum(t) / steps, 4), "median_ms": round(median(t), 4),
+                "p95_ms": round(t[min(steps - 1, int(math.ceil(0.95 * steps)) - 1)], 4),
+                "tflops_median": round(cfg.flops / (median(t) * 1e-3) / 1e12, 2)}
     plan = mm.mmrelu_plan(mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16, cfg.M, cfg.N, cfg.K,
                           cfg.lda, cfg.ldb, cfg.ldc)
-    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "plan": plan, "inputs": (a, b), "da": da, "db": db}
+    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "per_call": per_call, "plan": plan,
+            "inputs": (a, b), "da": da, "db": db, "c": c}
+
+
+def median(sorted_t):
+    n = len(sorted_t)
+    return sorted_t[n // 2] if n % 2 else 0.5 * (sorted_t[n // 2 - 1] + sorted_t[n // 2])
 
 
 def mfma_ceiling(da, db, steps, warmup, torch):
@@ -415,34 +436,81 @@ def row_stats(op, dtype, M, N, steps, warmup, torch, mm, datagen):
     return r
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, a, b, target_s, oracle):
     """The oracle timed on rows [0, r) of the workload, r chosen so that the
     timed part takes about target_s seconds: a calibration run on a few rows
     per thread, one correction if the timed run came out under half the
-    target, and whole-matrix repeats if even all rows take under 10 s."""
+    target, and whole-matrix repeats if even all rows take under 10 s.
+    Returns the baseline record and the oracle's rows [0, r) from the last
+    run (fp64), which the caller compares with the timed output."""
     def run(rows):
         t0 = time.perf_counter()
-        oracle.mmrelu(a, b, M=rows, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
-        return time.perf_counter() - t0
+        r = oracle.mmrelu(a, b, M=rows, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
+        return time.perf_counter() - t0, r
     clamp = lambda r: int(min(cfg.M, max(1, r)))
     cal_rows = clamp(max(64, 4 * oracle.num_threads()))
-    t_cal = run(cal_rows)
+    t_cal, _ = run(cal_rows)
     rows = clamp(target_s / max(t_cal, 1e-6) * cal_rows)
-    t = run(rows)
+    t, ref = run(rows)
     if t < 0.5 * target_s and rows < cfg.M:
         rows = clamp(rows * target_s / max(t, 1e-6))
-        t = run(rows)
+        del ref
+        t, ref = run(rows)
     reps = 1
     if rows == cfg.M and t < 10.0:
         reps = max(1, math.ceil(10.0 / max(t, 1e-6)))
-        t += sum(run(rows) for _ in range(reps - 1))
+        for _ in range(reps - 1):
+            del ref
+            dt, ref = run(rows)
+            t += dt
     flops = 2.0 * rows * cfg.N * cfg.K * reps
     what = f"rows 0..{rows - 1} of {cfg.M}" if rows < cfg.M else f"all {cfg.M} rows"
     times = f", computed {reps} times" if reps > 1 else ""
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{what} of the {cfg.name} workload ({rows}x{cfg.N} outputs, K={cfg.K}){times}, fp64 oracle, "
-                      f"{t:.1f} s in all"}
+    rec = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": f"{what} of the {cfg.name} workload ({rows}x{cfg.N} outputs, K={cfg.K}){times}, fp64 oracle, "
+                     f"{t:.1f} s in all"}
+    return rec, ref
+
+
+def parity_of(cfg, c_dev, ref, datagen):
+    """The timed output against the oracle's rows [0, r): fp32 max |C - R|
+    against 1e-4 sqrt(K); bf16 ||C - R||_F / ||R||_F against 1e-2, and the
+    largest element error over its bound 2^-8 |R| + 1e-6."""
+    import numpy as np
+    rows = ref.shape[0]
+    c = c_dev[:rows, :cfg.N]
+    if cfg.dtype == "bf16":
+        import torch
+        c = datagen.bf16_bits_to_f32(c.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    else:
+        c = c.cpu().numpy().astype(np.float64)
+    out = {"rows_compared": f"0..{rows - 1} of {cfg.M}", "elements": int(c.size),
+           "finite": bool(np.isfinite(c).all())}
+    d = np.abs(c - ref)
+    if cfg.dtype == "f32":
+        tol = 1e-4 * math.sqrt(cfg.K)
+        out.update({"metric": "max |C - R|", "value": float(d.max()), "tol": tol,
+                    "pass": bool(out["finite"] and d.max() <= tol)})
+    else:
+        rel = float(np.linalg.norm(c - ref) / np.linalg.norm(ref))
+        worst = float((d / (2.0 ** -8 * np.abs(ref) + 1e-6)).max())
+        out.update({"metric": "||C - R||_F / ||R||_F", "value": rel, "tol": 1e-2,
+                    "max_elem_err_over_bound": round(worst, 4),
+                    "pass": bool(out["finite"] and rel <= 1e-2 and worst <= 1.0)})
+    return out
 
 
 def main():
@@ -626,6 +694,7 @@ def main():
                    "M": head.M, "N": head.N, "K": head.K, "lda": head.lda, "ldb": head.ldb, "ldc": head.ldc,
                    "kernel": kernel, "grid": res["plan"]["grid"]},
         "pct_of_peak": round(100 * achieved / PEAK_TFLOPS["bf16"], 2),
+        "per_call": res["per_call"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic},
@@ -646,21 +715,35 @@ def main():
                                        "block on operands loaded from A and B; TFLOP/s per MFMA shape",
                                "unit": "TFLOP/s", **mc,
                                "value_frac_of_ceiling": round(achieved / mc["workload_16x16"], 4)}
+    r32 = None
     if not args.no_f32:
         f = datagen.CONFIGS[3]
         r32 = time_workload(f, args.steps, args.warmup, torch, mm, datagen)
         out["fp32_4096"] = {"value": round(r32["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r32["ms"], 4),
                             "frac": round(r32["tflops"] / PEAK_TFLOPS["f32"], 4), "peak": PEAK_TFLOPS["f32"],
-                            "kernel": r32["plan"]["name"],
+                            "kernel": r32["plan"]["name"], "per_call": r32["per_call"],
                             "traffic": measured_traffic("f32", r32["plan"]["name"])}
     if args.calib_copy_mib > 0:
         out["calib_copy_bytes"] = calib_copy(args.calib_copy_mib, torch)
     if not args.no_cpu_baseline:
+        # The oracle on this host's cores: timed as the CPU baseline, and its
+        # result compared with the output of the timed calls.
         import oracle
         a, b = res["inputs"]
-        out["cpu_baseline"] = cpu_baseline(head, a, b, args.cpu_seconds, oracle)
+        out["cpu_baseline"], ref = cpu_baseline(head, a, b, args.cpu_seconds, oracle)
+        out["parity"] = parity_of(head, res["c"], ref, datagen)
+        del ref
+        if r32 is not None:
+            # fp32: the first rows of its output, about two seconds of oracle work
+            a32, b32 = r32["inputs"]
+            t0 = time.perf_counter()
+            probe = oracle.mmrelu(a32, b32, M=64, N=f.N, K=f.K, lda=f.lda, ldb=f.ldb)
+            rows = int(min(f.M, max(64, 64 * 2.0 / max(time.perf_counter() - t0, 1e-6))))
+            ref32 = probe if rows == 64 else oracle.mmrelu(a32, b32, M=rows, N=f.N, K=f.K, lda=f.lda, ldb=f.ldb)
+            out["fp32_4096"]["parity"] = parity_of(f, r32["c"], ref32, datagen)
     else:
         out["cpu_baseline"] = None
+        out["parity"] = None
     print(json.dumps(out), flush=True)
 
 

@@ -28,7 +28,14 @@
  * overlap A or B (not checked).
  *
  * Errors: arguments are checked BEFORE anything is enqueued; on any non-zero
- * status nothing has been launched and C is untouched.
+ * status nothing has been launched and C is untouched. This follows the host
+ * wrapper of the diy-llm chapter ("Chapter 7: GPU High-Performance
+ * Programming", section 7.4.3, writing kernels with the C++ API): before the
+ * launch the wrapper checks that its input is device memory laid out the way
+ * the kernel indexes it, the caller-side output is written without being
+ * cleared first, and the launch itself is checked right after it is issued.
+ * Here the layout check is the leading-dimension and alignment rules below,
+ * and the launch check is hipGetLastError.
  *   MMRELU_ERR_INVALID_VALUE  M, N or K negative; lda < max(1,K), ldb < max(1,N),
  *                             ldc < max(1,N); or a size past the limits below.
  *   MMRELU_ERR_NULL_POINTER   C null (M, N > 0), or A/B null (M, N, K > 0).
@@ -43,7 +50,11 @@
  * writes C = 0 (the K loop runs zero times and relu(0) is stored).
  *
  * Limits: M, N, K <= 2^31 - 1 and lda, ldb, ldc <= 2^21 elements (the kernels
- * address each tile with 32-bit offsets from a 64-bit tile base).
+ * address each tile with 32-bit offsets from a 64-bit tile base), and one
+ * launch holds fewer than 2^32 work-items: the planned grid times the
+ * kernel's threads per workgroup (mmrelu_plan reports both) must stay below
+ * 2^32, else MMRELU_ERR_INVALID_VALUE. That bounds only extreme shapes, e.g.
+ * N = 1 runs one 256-thread workgroup per four rows, so M < 2^26 rows.
  */
 #ifndef MMRELU_H
 #define MMRELU_H
@@ -227,7 +238,7 @@ typedef struct {
  *     smallest row count that covers M (16, 32 or 64 rows; it splits K over
  *     the eight waves of a workgroup so a 32-column strip of B streams from
  *     memory once); M <= 16 with at least one 64-column strip per CU takes
- *     64-column strips (fp32 variant 13, bf16 variant 15);
+ *     64-column strips (fp32 variant 13, bf16 variant 14);
  *   - an aligned layout with N <= 64: the skinny-N kernel of the smallest
  *     column count that covers N (16, 32 or 64), over 32-row bands of A;
  *     fp32 with N <= 16 and at least one 64-row band per CU takes 64-row
@@ -238,14 +249,13 @@ typedef struct {
  *     kernel left with one tile per CU, which then runs latency-bound).
  *     Candidates: the dtype's matrix-core kernels at a large and a small
  *     tile that accept the layout (aligned bf16: the 256 x 256 ping-pong
- *     tile with 64-deep intervals, variant 17, the 128 x 128 tile, variant
- *     4, and the 128 x 256 ping-pong tile, variant 18) and, for aligned
- *     layouts, the seven
+ *     tile, variant 1, the 128 x 256 ping-pong tile, variant 3, and the
+ *     128 x 128 tile, variant 4) and, for aligned layouts, the seven
  *     skinny tiles (variants 5 - 10 and the 64 x 64 variant 12), which split
  *     K over eight waves and keep every CU busy when the large tiles cannot
  *     (small squares, long K with few output tiles); other layouts run the
  *     fp32 unaligned matrix-core kernels, or for bf16 the any-layout
- *     matrix-core kernel: 128 x 128 tiles (variant 14) when that grid gives
+ *     matrix-core kernel: 128 x 128 tiles (variant 2) when that grid gives
  *     every CU at least one tile, else 64 x 64 tiles (variant 13).
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,

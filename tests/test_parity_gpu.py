@@ -11,10 +11,14 @@ path through the C-ABI, and compares with the oracle on the same inputs:
     magnitudes), and exact equality with round-to-nearest-even of the oracle
     on small-integer inputs.
 Small shapes span several tiles with ragged tails and are compared element
-by element; the five full-size workloads run in the configuration the
-benchmark times and are compared on sampled rows, columns and entries that
-the oracle evaluates one by one, plus properties that hold at any size.
+by element. The five full-size workloads run in the configuration the
+benchmark times and every element of C is compared with the oracle, which
+is evaluated one block of rows at a time; their shapes and leading
+dimensions are also run on small-integer inputs, compared bit for bit. The
+planner's tile kernels run multi-band ragged grids (the per-XCD regroup and
+several bands of tile rows) element by element, and repeat bit for bit.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -205,9 +209,9 @@ def placed(x: np.ndarray, off: int, ld: int):
 # (dtype, element offsets of A, B, C, variants). Only element alignment is
 # required of pointers; these start A, B and C 1..7 elements past a 16-byte
 # boundary, through the planner (None) and the kernels that accept such
-# layouts: bf16 13/14 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
+# layouts: bf16 2/13 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
 # 11 (matrix-vector) and 0.
-MISALIGNED = [("bf16", (1, 3, 5), [None, 13, 14, 0]), ("bf16", (7, 2, 0), [None, 13, 14]),
+MISALIGNED = [("bf16", (1, 3, 5), [None, 2, 13, 0]), ("bf16", (7, 2, 0), [None, 2, 13]),
               ("bf16", (0, 0, 3), [None, 13]), ("f32", (1, 2, 3), [None, 2, 4, 0]), ("f32", (3, 0, 1), [None, 2, 4])]
 
 
@@ -304,7 +308,9 @@ def test_empty_outputs_launch_nothing():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_deterministic_repeats(dtype):
-    """No atomics: 20 runs must agree bit for bit (a proxy for LDS races)."""
+    """No atomics: 20 runs must agree bit for bit (a proxy for LDS races);
+    this shape runs a skinny kernel, whose eight waves sum their partial
+    tiles through LDS."""
     M, N, K = 512, 512, 1024
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     a = to_dev(datagen.normal_f32(81, M, K, 1 / math.sqrt(K))).to(tdt)
@@ -312,6 +318,29 @@ def test_deterministic_repeats(dtype):
     first = mm.mmrelu(a, b).clone()
     for _ in range(19):
         assert torch.equal(mm.mmrelu(a, b), first)
+
+
+# (dtype, variant, shape): the tile kernels on grids of several waves. bf16 1
+# and 3 are the ping-pong tiles (an LDS ring per operand, the two wave
+# groups swapping roles at every barrier), 4 the 128 x 128 tile; fp32 1 the
+# aligned 128 x 128 tile, 4 the unaligned 64 x 64 tile.
+DETERMINISM = [("bf16", 1, (4352, 4352, 520)), ("bf16", 3, (4352, 4352, 520)), ("bf16", 4, (4352, 4352, 520)),
+               ("f32", 1, (4352, 4352, 264)), ("f32", 4, (4352, 4352, 264))]
+
+
+@pytest.mark.parametrize("dtype,variant,shape", DETERMINISM, ids=[f"{d}-v{v}" for d, v, _ in DETERMINISM])
+def test_tile_kernels_deterministic_repeats(dtype, variant, shape):
+    M, N, K = shape
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    plan = mm.mmrelu_plan_variant(kind, variant, M, N, K, K, N, N)
+    assert plan["waves"] >= 2, plan                 # more tiles than one round of the CUs holds
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    a = to_dev(datagen.normal_f32(83, M, K, 1 / math.sqrt(K))).to(tdt)
+    b = to_dev(datagen.normal_f32(84, K, N, 1 / math.sqrt(K))).to(tdt)
+    print(f"determinism {dtype} variant={variant} {M}x{N}x{K}", flush=True)
+    first = mm.mmrelu(a, b, variant=variant).clone()
+    for _ in range(19):
+        assert torch.equal(mm.mmrelu(a, b, variant=variant), first)
 
 
 def test_torch_wrapper_row_strided_out():
@@ -326,40 +355,190 @@ def test_torch_wrapper_row_strided_out():
     assert torch.all(big[:, N:] == -1.0)
 
 
+def test_torch_wrapper_single_column_of_any_stride():
+    """A (K, 1) view of a (1, K) tensor has column stride K, which a single
+    column never uses: the wrapper takes it as row-major with ld 1."""
+    M, K = 200, 136
+    a = datagen.normal_f32(93, M, K)
+    b = datagen.normal_f32(94, 1, K)
+    col = to_dev(b).t()
+    assert col.shape == (K, 1) and col.stride() == (1, K)
+    c = mm.mmrelu(to_dev(a), col)
+    torch.cuda.synchronize()
+    check_f32(c.cpu().numpy(), oracle.mmrelu(a, np.ascontiguousarray(b.T)), K)
+
+
 # --- the five workloads at full size -----------------------------------------
 
-def sample_indices(M, N, seed, rows=6, cols=6, points=4000):
-    """Whole rows (first, last, random), whole columns (likewise) and random
-    entries of an M x N output, as flat (row, col) index arrays."""
-    rng = np.random.default_rng(seed)
-    rsel = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, rows)]))
-    csel = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, cols)]))
-    ii = np.concatenate([np.repeat(rsel, N), np.tile(np.arange(M), csel.size), rng.integers(0, M, points)])
-    jj = np.concatenate([np.tile(np.arange(N), rsel.size), np.repeat(csel, M), rng.integers(0, N, points)])
-    return ii, jj
+def oracle_row_blocks(a, b, M, N, K, lda, ldb, rows=512):
+    """The oracle over the whole M x N output, one block of rows at a time
+    (the 8192 x 8192 result in fp64 would take 512 MB): yields (i0, i1,
+    R[i0:i1])."""
+    for i0 in range(0, M, rows):
+        i1 = min(M, i0 + rows)
+        yield i0, i1, oracle.mmrelu(a[i0:i1], b, M=i1 - i0, N=N, K=K, lda=lda, ldb=ldb)
 
 
 @pytest.mark.parametrize("ident", [1, 2, 3, 4, 5])
 def test_workload_full_size(ident):
+    """The workload as the benchmark runs it (planner's kernel, the config's
+    leading dimensions), into a NaN-filled C with guard rows; every element
+    is compared with the oracle: fp32 max |C - R| <= 1e-4 sqrt(K), bf16
+    ||C - R||_F / ||R||_F <= 1e-2 over the whole output plus the element-wise
+    bound."""
     cfg = datagen.CONFIGS[ident]
     print(f"workload {cfg.name}", flush=True)
     a, b = datagen.make_inputs(cfg)
-    c, _ = run(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, ldc=cfg.ldc)
-    if cfg.M * cfg.N * cfg.K <= 1024 ** 3:
-        r = oracle.mmrelu(a, b, M=cfg.M, N=cfg.N, K=cfg.K, lda=cfg.lda, ldb=cfg.ldb)
-        cs, rs = c, r
-    else:
-        ii, jj = sample_indices(cfg.M, cfg.N, 1000 + ident)
-        rs = oracle.mmrelu_at(a, b, ii, jj, cfg.K, cfg.lda, cfg.ldb)
-        cs = c[ii, jj]
-    if cfg.dtype == "f32":
-        check_f32(cs, rs, cfg.K)
-        cfull = c
-    else:
-        check_bf16(cs, rs)
-        cfull = datagen.bf16_bits_to_f32(c)
-    # any-size properties over the whole output: finite, non-negative, and
-    # for inputs symmetric about 0 about half the outputs are exactly zero
-    assert np.all(np.isfinite(cfull)) and np.all(cfull >= 0)
-    frac = float(np.mean(cfull == 0))
+    c, whole = run(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, ldc=cfg.ldc, guard=2)
+    num = den = worst = 0.0
+    zeros = 0
+    for i0, i1, r in oracle_row_blocks(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb):
+        if cfg.dtype == "f32":
+            blk = c[i0:i1]
+            check_f32(blk, r, cfg.K)
+            worst = max(worst, float(np.abs(blk.astype(np.float64) - r).max()))
+        else:
+            blk = datagen.bf16_bits_to_f32(c[i0:i1])
+            cb = blk.astype(np.float64)
+            assert np.all(np.isfinite(cb)) and np.all(cb >= 0)
+            d = cb - r
+            num += float(np.sum(d * d))
+            den += float(np.sum(r * r))
+            assert np.all(np.abs(d) <= 2.0 ** -8 * np.abs(r) + 1e-6), f"rows {i0}..{i1}: {np.abs(d).max()}"
+        zeros += int(np.count_nonzero(blk == 0))
+    if cfg.dtype == "bf16":
+        worst = math.sqrt(num / den)
+        assert worst <= 1e-2, f"relative Frobenius error {worst}"
+    print(f"workload {cfg.name}: {'max abs' if cfg.dtype == 'f32' else 'rel Frobenius'} error {worst:.3g}", flush=True)
+    # nothing outside C's rows was written
+    rest = np.concatenate([whole[:2], whole[2 + cfg.M:]])
+    rest = rest if cfg.dtype == "f32" else datagen.bf16_bits_to_f32(rest)
+    assert np.all(np.isnan(rest))
+    # inputs symmetric about 0: about half the outputs are exactly zero
+    frac = zeros / (cfg.M * cfg.N)
     assert abs(frac - 0.5) < 0.01, frac
+
+
+def small_int_inputs(cfg, seed):
+    """Integers in [-4, 4] of the config's shape and leading dimensions, in
+    its dtype: every partial sum is an integer below 16 K <= 2^17, exact in
+    fp32 in any order."""
+    a = datagen.small_int_f32(seed, cfg.M, cfg.K)
+    b = datagen.small_int_f32(seed + 1, cfg.K, cfg.N)
+    if cfg.dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a), datagen.f32_to_bf16_bits(b)
+    return datagen.pad_rows(a, cfg.lda), datagen.pad_rows(b, cfg.ldb)
+
+
+# (config, dtype, variant): the workloads' shapes and leading dimensions on
+# small-integer inputs, through the planner (None) and, for the ragged shape
+# with odd leading dimensions, every kernel that accepts that layout: fp32 2
+# and 4 (unaligned 128 and 64 tiles), bf16 2 and 13 (any-layout 128 and 64
+# tiles), and the plain kernel 0.
+EXACT = [(1, "f32", None), (2, "f32", None), (3, "f32", None), (4, "f32", None), (4, "f32", 2), (4, "f32", 4),
+         (4, "f32", 0), (4, "bf16", None), (4, "bf16", 13), (4, "bf16", 0), (5, "bf16", None)]
+
+
+@pytest.mark.parametrize("ident,dtype,variant", EXACT, ids=[f"C{i}-{d}-v{v}" for i, d, v in EXACT])
+def test_workload_shapes_exact_integers(ident, dtype, variant):
+    """Bit-exact parity at the workload shapes: fp32 C equals the oracle, bf16
+    C equals its round-to-nearest-even (C4: lda 2049 and ldb = ldc = 3001,
+    rows on every 4- or 2-byte boundary; C5: 8192^3 with results up to 2^17,
+    which need bf16 rounding)."""
+    cfg = dataclasses.replace(datagen.CONFIGS[ident], dtype=dtype)
+    print(f"exact {cfg.name} as {dtype} variant={variant}", flush=True)
+    a, b = small_int_inputs(cfg, 3000 + 10 * ident)
+    c, whole = run(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, ldc=cfg.ldc, variant=variant, guard=2)
+    big = 0.0
+    for i0, i1, r in oracle_row_blocks(a, b, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb):
+        if dtype == "f32":
+            np.testing.assert_array_equal(c[i0:i1].astype(np.float64), r, err_msg=f"rows {i0}..{i1}")
+        else:
+            np.testing.assert_array_equal(c[i0:i1], bf16_round_ref(r), err_msg=f"rows {i0}..{i1}")
+        big = max(big, float(r.max()))
+    if dtype == "bf16":
+        assert big > 256                          # the results need bf16 rounding
+    rest = np.concatenate([whole[:2], whole[2 + cfg.M:]])
+    rest = rest if dtype == "f32" else datagen.bf16_bits_to_f32(rest)
+    assert np.all(np.isnan(rest))
+
+
+# --- the tile kernels' grid mapping, element by element ------------------------
+
+def run_fused(act, a, b, bias, M, N, K, variant):
+    """act(A·B + bias) through the fused C entry point with an explicit
+    variant, into a NaN-filled C."""
+    dt = torch.float32 if a.dtype == np.float32 else torch.bfloat16
+    da, db = to_dev(a), to_dev(b)
+    dbias = to_dev(bias) if bias is not None else None
+    c = torch.full((M, N), float("nan"), dtype=dt, device="cuda")
+    code = {"relu": mm.ACT_RELU, "gelu_tanh": mm.ACT_GELU_TANH, "none": mm.ACT_NONE}[act]
+    args = (variant, code, da.data_ptr(), db.data_ptr(), dbias.data_ptr() if dbias is not None else 0,
+            c.data_ptr(), M, N, K, K, N, N, torch.cuda.current_stream().cuda_stream)
+    fn = mm.mmrelu_fused_f32_variant if dt == torch.float32 else mm.mmrelu_fused_bf16_variant
+    rc = fn(*args)
+    assert rc == mm.MMRELU_OK, mm.status_string(rc)
+    torch.cuda.synchronize()
+    return to_host(c)
+
+
+# 2312 x 2320 x 200: ragged in all three dimensions (the last tile row holds
+# 8 rows, the last tile column 16 columns, the last 64-deep pair of slabs 8 k)
+# and a grid of several bands of tile rows, with more tiles than XCDs and a
+# tile count that is not a multiple of eight (so both the regrouped ids and
+# the tail walk their bands). bf16: 1, 3 ping-pong tiles, 4 the 128 x 128
+# tile; fp32: 1, 2 the 128 x 128 tiles, 3, 4 the 64 x 64 tiles.
+MULTIBAND = (2312, 2320, 200)
+TILE_KERNELS = [("bf16", 1), ("bf16", 3), ("bf16", 4), ("f32", 1), ("f32", 2), ("f32", 3), ("f32", 4)]
+EPILOGUES = [("relu", False), ("gelu_tanh", True), ("none", True)]
+
+
+@pytest.mark.parametrize("act,with_bias", EPILOGUES, ids=[f"{a}-{'bias' if b else 'nobias'}" for a, b in EPILOGUES])
+@pytest.mark.parametrize("dtype,variant", TILE_KERNELS, ids=[f"{d}-v{v}" for d, v in TILE_KERNELS])
+def test_tile_kernels_multiband_ragged(dtype, variant, act, with_bias):
+    """Every element of a multi-band ragged product through one tile kernel,
+    against the oracle's fused form (tolerances of the fused-epilogue tests:
+    fp32 |C - R| <= L 1e-4 sqrt(K) + 2e-6 (1 + |R|), L = 1.13 for GeLU;
+    bf16 relative Frobenius 1e-2 and |C - R| <= 2^-8 |R| + 4e-6)."""
+    M, N, K = MULTIBAND
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    plan = mm.mmrelu_plan_variant(kind, variant, M, N, K, K, N, N)
+    assert plan["tiles_m"] > 8 and plan["grid"] >= 16 and plan["grid"] % 8 != 0, plan
+    a = datagen.normal_f32(3100 + variant, M, K, 1 / math.sqrt(K))
+    b = datagen.normal_f32(3200 + variant, K, N, 1 / math.sqrt(K))
+    bias = datagen.normal_f32(3300 + variant, 1, N, 0.5).ravel() if with_bias else None
+    if dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a), datagen.f32_to_bf16_bits(b)
+        bias = datagen.f32_to_bf16_bits(bias) if bias is not None else None
+    print(f"multiband {dtype} variant={variant} act={act} bias={with_bias}", flush=True)
+    c = run_fused(act, a, b, bias, M, N, K, variant)
+    r = oracle.fused(act, a, b, bias)
+    if dtype == "f32":
+        assert np.all(np.isfinite(c))
+        slope = 1.13 if act == "gelu_tanh" else 1.0
+        err = np.abs(c.astype(np.float64) - r)
+        assert np.all(err <= slope * 1e-4 * math.sqrt(K) + 2e-6 * (1 + np.abs(r))), err.max()
+    else:
+        cf = datagen.bf16_bits_to_f32(c).astype(np.float64)
+        assert np.all(np.isfinite(cf))
+        assert np.linalg.norm(cf - r) / np.linalg.norm(r) <= 1e-2
+        assert np.all(np.abs(cf - r) <= 2.0 ** -8 * np.abs(r) + 4e-6), np.abs(cf - r).max()
+
+
+@pytest.mark.parametrize("dtype,variant", TILE_KERNELS, ids=[f"{d}-v{v}" for d, v in TILE_KERNELS])
+def test_tile_kernels_multiband_exact_integers(dtype, variant):
+    """The same grids on small-integer inputs: bit-exact (bf16: the oracle
+    rounded to nearest-even), so a tile written to the wrong place, or a
+    wrong slab summed into a right one, cannot hide under a tolerance."""
+    M, N, K = MULTIBAND
+    a = datagen.small_int_f32(3400 + variant, M, K)
+    b = datagen.small_int_f32(3500 + variant, K, N)
+    if dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a), datagen.f32_to_bf16_bits(b)
+    print(f"multiband exact {dtype} variant={variant}", flush=True)
+    c = run_fused("relu", a, b, None, M, N, K, variant)
+    r = oracle.mmrelu(a, b)
+    if dtype == "f32":
+        np.testing.assert_array_equal(c.astype(np.float64), r)
+    else:
+        np.testing.assert_array_equal(c, bf16_round_ref(r))

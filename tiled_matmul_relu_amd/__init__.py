@@ -283,14 +283,17 @@ def mmrelu_wave_quantization(blocks: int, slots: int) -> tuple[int, int]:
 
 # --- torch convenience wrapper ----------------------------------------------
 
+def _row_major(t) -> bool:
+    """2-D with unit column stride and rows that do not overlap; a single
+    column's stride is never used, so any value is accepted for it."""
+    return t.dim() == 2 and (t.stride(1) == 1 or t.shape[1] <= 1) and t.stride(0) >= max(t.shape[1], 1)
+
+
 def _ld(t) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    """Leading dimension (elements) of a tensor that _row_major accepts."""
+    if not _row_major(t):
         raise ValueError("matrices must be 2-D, row-major with unit column stride")
     return max(t.stride(0), t.shape[1], 1)
-
-
-def _row_major(t) -> bool:
-    return t.dim() == 2 and (t.stride(1) == 1 or t.shape[1] <= 1) and t.stride(0) >= max(t.shape[1], 1)
 
 
 def mmrelu(a, b, out=None, variant: int | None = None, stream=None, bias=None, act: str = "relu"):

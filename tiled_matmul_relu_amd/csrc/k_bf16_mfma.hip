@@ -6,9 +6,9 @@
 // The lecture's tiled recipe (one workgroup per output tile; K swept in slabs
 // staged in on-chip memory; fp32 accumulator; the activation on the
 // accumulator right before the single, masked store), laid out for CDNA4:
-//  * 256 x 256 output tile per workgroup of 4 wave64s (2 x 2); each wave owns
-//    a 128 x 128 sub-tile: 64 16x16 MFMA blocks, 256 fp32 accumulators per
-//    lane held in AGPRs (one wave per SIMD).
+//  * 128 x 128 output tile per workgroup of 4 wave64s (2 x 2); each wave owns
+//    a 64 x 64 sub-tile: 16 16x16 MFMA blocks, 64 fp32 accumulators per
+//    lane; two workgroups per CU.
 //  * K slabs of 32 are copied global -> LDS by the buffer unit directly (no
 //    VGPR round trip) into a ring of STAGES buffers, STAGES-1 slabs ahead of
 //    the multiply, which hides the latency of copies that miss L2. Lanes
@@ -27,6 +27,8 @@
 //    4*(s%4) .. +3, and two such reads give the 8 k values of column t. B rows
 //    are XOR swizzled so the 16 rows touched by one such read spread over
 //    the banks.
+//  * Fragments are double-buffered in registers: while the MFMAs of slab kt
+//    run, the fragments of slab kt+1 are read from LDS.
 //  * With B as the first MFMA operand, a lane's four accumulators are four
 //    consecutive columns of one row of C: the epilogue writes 8 bytes a lane.
 // Requires lda, ldb, ldc, K and N to be multiples of 8 and 16-byte aligned
@@ -67,7 +69,7 @@ struct Bf16Tile {
 // full rate on gfx950).
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
 
     // Two register sets of MFMA operands: while the MFMAs of slab kt run, the
     // fragments of slab kt+1 are read from LDS.
-    bf16x8 fa[PREFETCH ? 2 : 1][T::MB], fb[PREFETCH ? 2 : 1][T::NB];
+    bf16x8 fa[2][T::MB], fb[2][T::NB];
     // Fragment reads of one 16-row A block (c < MB) or one 16-column B block
     // (c < NB) of a stage into register set `set`.
     auto load_frag_a = [&](int set, int stage, int c) __attribute__((always_inline)) {
@@ -241,41 +243,22 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     };
 
     const int nk = (K + BK - 1) / BK;
-    if constexpr (PREFETCH) {
-        if (nk > 0) {
+    if (nk > 0) {
 #pragma unroll
-            for (int s = 0; s < STAGES; ++s) issue_loads(s, s * BK);
-            wait_vmcnt<(STAGES - 1) * T::kLoads>();
-            __syncthreads();
-            load_frags(0, 0);
-            int kt = 0;
-            for (; kt + 2 < nk; kt += 2) {
-                step(kt, 0);
-                step(kt + 1, 1);
-            }
-            if (kt + 1 < nk) {
-                step(kt, 0);
-                mfmas(1);
-            } else {
-                mfmas(0);
-            }
+        for (int s = 0; s < STAGES; ++s) issue_loads(s, s * BK);
+        wait_vmcnt<(STAGES - 1) * T::kLoads>();
+        __syncthreads();
+        load_frags(0, 0);
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {
+            step(kt, 0);
+            step(kt + 1, 1);
         }
-    } else {
-        // Two waves per SIMD: one register set of fragments; while one wave
-        // waits for its fragment reads the other wave's MFMAs run. Step kt:
-        // wait for slab kt (slabs kt+1 .. kt+STAGES-2 may stay in flight),
-        // barrier (every wave is done with slab kt-1, so its stage is free),
-        // refill that stage with slab kt+STAGES-1, read slab kt, multiply.
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) issue_loads(s, s * BK);
-        for (int kt = 0; kt < nk; ++kt) {
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<(STAGES - 2) * T::kLoads>();
-            __syncthreads();
-            issue_loads((kt + STAGES - 1) & (STAGES - 1), (kt + STAGES - 1) * BK);
-            load_frags(0, kt & (STAGES - 1));
+        if (kt + 1 < nk) {
+            step(kt, 0);
+            mfmas(1);
+        } else {
             mfmas(0);
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -319,11 +302,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, 1) void mmrelu_bf16_mfma(
     });
 }
 
-template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool PREFETCH, int GROUP_M>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, int GROUP_M>
 hipError_t launch_bf16(const Problem &p, int64_t grid, hipStream_t stream)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    hipLaunchKernelGGL((mmrelu_bf16_mfma<BM, BN, BK, STAGES, WAVES_M, WAVES_N, PREFETCH>), dim3(static_cast<uint32_t>(grid)),
+    hipLaunchKernelGGL((mmrelu_bf16_mfma<BM, BN, BK, STAGES, WAVES_M, WAVES_N>), dim3(static_cast<uint32_t>(grid)),
                        dim3(WAVES_M * WAVES_N * 64), 0, stream, static_cast<const uint16_t *>(p.A),
                        static_cast<const uint16_t *>(p.B), static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda,
                        p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M, static_cast<const uint16_t *>(p.bias), p.act);
@@ -332,27 +315,13 @@ hipError_t launch_bf16(const Problem &p, int64_t grid, hipStream_t stream)
 
 }  // namespace
 
-const Variant *variant_bf16_mfma256()
-{
-    static const Variant v = {"mmrelu_bf16_mfma<256,256,32,4,2,2,prefetch>", MMRELU_DTYPE_BF16, 256, 256, 32, 256, 1, 8,
-                              launch_bf16<256, 256, 32, 4, 2, 2, true, 4>};
-    return &v;
-}
-const Variant *variant_bf16_mfma256_8w()
-{
-    static const Variant v = {"mmrelu_bf16_mfma<256,256,32,4,2,4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_bf16<256, 256, 32, 4, 2, 4, false, 4>};
-    return &v;
-}
-
 // 128 x 128 tiles (2 x 2 waves of 64 x 64): four times the workgroups of the
 // 256 x 256 tile, for shapes whose 256 x 256 grid leaves most CUs idle.
-// Relative cost per output 1.66 against the 64-deep 256 x 256 ping-pong tile
-// (1.55 against the 32-deep one, times its speedup 1.067).
+// Relative cost per output 1.66 against the 256 x 256 ping-pong tile.
 const Variant *variant_bf16_mfma128()
 {
-    static const Variant v = {"mmrelu_bf16_mfma<128,128,32,4,2,2,prefetch>", MMRELU_DTYPE_BF16, 128, 128, 32, 256, 2, 8,
-                              launch_bf16<128, 128, 32, 4, 2, 2, true, 8>, 1.66f};
+    static const Variant v = {"mmrelu_bf16_mfma<128,128,32,4,2,2>", MMRELU_DTYPE_BF16, 128, 128, 32, 256, 2, 8,
+                              launch_bf16<128, 128, 32, 4, 2, 2, 8>, 1.66f};
     return &v;
 }
 

@@ -1,10 +1,10 @@
 // bf16 relu(A·B) on the gfx950 matrix cores, "ping-pong" schedule: eight
-// wave64s per 256 x 256 output tile, two on each SIMD, split into two groups
-// of four. Between two consecutive barriers one group only runs MFMAs while
-// the other only reads operand fragments from LDS and issues global->LDS
-// copies; at the barrier the roles swap. Each SIMD therefore always has one
-// wave feeding its matrix core and one wave doing memory work, and the
-// hardware issues both streams side by side.
+// wave64s per output tile (256 x 256, or 128 x 256), two on each SIMD, split
+// into two groups of four. Between two consecutive barriers one group only
+// runs MFMAs while the other only reads operand fragments from LDS and issues
+// global->LDS copies; at the barrier the roles swap. Each SIMD therefore
+// always has one wave feeding its matrix core and one wave doing memory work,
+// and the hardware issues both streams side by side.
 //
 // The arithmetic is the lecture's tiled matmul with the fused activation
 // ("Kernels, Triton, XLA", section "Reductions and tiling", and the Chinese
@@ -15,47 +15,33 @@
 // masked store.
 //
 // Waves: wave w belongs to group w / 4; within a group, (wm, wn') =
-// ((w%4)/2, (w%4)%2) and the wave owns rows 128*wm .. +128 and columns
-// 64*(wn' + 2*group) .. +64 of the tile (8 x 4 MFMA blocks, 128 fp32
-// accumulators per lane). Slabs are 32 deep along K.
+// ((w%4)/2, (w%4)%2) and the wave owns rows (BM/2)*wm .. +BM/2 and columns
+// 64*(wn' + 2*group) .. +64 of the tile (BM/32 x 4 MFMA blocks; 128 fp32
+// accumulators per lane for the 256-row tile). Slabs are 32 deep along K and
+// every interval between two barriers covers a PAIR of slabs, 64 k.
 //
-// LDS (160 KB): A is staged per PAIR of slabs (64 k, 128 bytes per row) in a
-// ring of three 32 KB stages, B per slab in a ring of four 16 KB stages.
+// LDS: A is staged per pair of slabs (64 k, 128 bytes per row) in a ring of
+// three stages (BM x 128 bytes each), B per slab in a ring of four 16 KB
+// stages (160 KB in all for the 256-row tile).
 //  - A stage: row r's 16-byte chunk c sits at r*128 + 16*(c ^ (r%8)). One
 //    copy instruction moves 8 rows x 128 bytes: lane 8r'+j fetches chunk
 //    j ^ r' of its row, so each group of 8 lanes reads one whole 128-byte
-//    line from global memory and writes it, permuted, to one LDS row. (With
-//    32-deep A slabs a row contributes only 64 bytes, and the global reads
-//    touch every line twice.) A fragment reads (16 lanes: 16 rows, one chunk)
-//    hit 16 distinct chunk positions and run at the full LDS rate.
+//    line from global memory and writes it, permuted, to one LDS row. A
+//    fragment reads (16 lanes: 16 rows, one chunk) hit 16 distinct chunk
+//    positions and run at the full LDS rate.
 //  - B stage: 32 rows of 512 bytes, 16-byte chunks XOR-swizzled by row, read
 //    with ds_read_b64_tr_b16 (each lane gets 8 consecutive k of a column).
-// Group 1 copies A, group 0 copies B; every wave issues four 1 KB copies per
-// memory interval.
+// Group 1 copies A, group 0 copies B; per interval every wave of group 0
+// issues eight 1 KB copies (two B slabs), every wave of group 1 BM/32 (the
+// A pair).
 //
-// Schedule (interval I_t ends at a barrier):
-//   prologue: group 1 copies A pairs 0 and 1, group 0 B slabs 0..2; wait for
-//             slab 0; barrier. I_-1: group 0 reads slab 0, copies B slab 3.
-//   I_2k:   group 0 multiplies slab k;
-//           group 1 reads slab k and copies half (k%2) of A pair (k+4)/2.
-//           Both then wait for their copies issued two memory intervals
-//           earlier (vmcnt(8)), which completes slab k+1.
-//   I_2k+1: group 0 reads slab k+1 and copies B slab k+4;
-//           group 1 multiplies slab k.
-// A pair p's stage last held pair p-3, whose second slab group 1 read in
-// I_4p-10; B slab m's stage last held slab m-4, read by group 1 in I_2m-8.
-// Copies past K are fully masked (they zero-fill stages that are never
-// read), so every interval costs the same vmcnt count and the loop has no
-// data-dependent branches.
+// Why 64-deep intervals: a memory interval's fragment reads take longer than
+// 32 MFMAs (about 640 cycles against 512, measured on a register-and-LDS
+// probe), so one slab per interval would leave the matrix cores idle at
+// every barrier; 64 MFMAs cover the reads of two slabs, and the barriers
+// halve. The memory role holds both slabs' fragments in two register sets.
 //
-// Deep intervals (DEPTH = 2): each interval covers a PAIR of slabs, 64 k.
-// The MFMA role issues 64 MFMAs per interval instead of 32, and the memory
-// role reads both slabs' fragments (two register sets) and issues the
-// pair's copies. The LDS layout and rings are the same. A memory interval's
-// fragment reads take longer than 32 MFMAs (about 640 cycles against 512,
-// measured on a register-and-LDS probe), so the 32-deep schedule leaves
-// the matrix cores idle at every barrier; 64 MFMAs cover the reads, and the
-// barriers halve. Schedule (J_t ends at a barrier; pair p = slabs 2p, 2p+1):
+// Schedule (J_t ends at a barrier; pair p = slabs 2p, 2p+1):
 //   prologue: group 1 copies A pairs 0 and 1, group 0 B pair 0; wait for
 //             pair 0; barrier. J_-1: group 0 reads pair 0, copies B pair 1.
 //   J_2p:   group 0 multiplies pair p, then waits for all its copies (B
@@ -66,6 +52,9 @@
 //           of pair p, which group 1 read in J_2p);
 //           group 1 multiplies pair p.
 // A pair p+2's stage last held pair p-1, read by group 1 in J_2p-2.
+// Copies past K are fully masked (they zero-fill stages that are never
+// read), so every interval costs the same vmcnt count and the loop has no
+// data-dependent branches.
 //
 // Requires lda, ldb, ldc, K and N to be multiples of 8 and 16-byte aligned
 // pointers.
@@ -101,7 +90,7 @@ struct PingPong {
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
-template <int BM, int ORDER, int DEPTH>
+template <int BM>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C,
     int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m,
@@ -111,8 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     constexpr int kMB = P::kMB, kStageABytes = P::kStageABytes, kBBase = P::kBBase, kCopies = P::kCopies;
     constexpr int kHalf = BM / 2;                      // rows per half of an A pair, and per wave
     static_assert(P::kLdsBytes <= 160 * 1024, "LDS budget");
-    static_assert(ORDER != 4 || BM == 256, "the MFMA role issues two copies per column block");
-    static_assert(DEPTH == 1 || (DEPTH == 2 && ORDER == 2), "slabs per interval; deep intervals pair copies and reads");
+    static_assert(kNB == kCopies, "one copy per fragment part");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[P::kLdsBytes / 2];
 
     const int lane = threadIdx.x & 63;
@@ -151,13 +139,15 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
             voff1[q] = kOutOfRange;
         }
     }
-    // Copy q of half hh of A pair p (group 1); the 128-row tile has two
-    // copies per half (q >= 2 issues nothing).
-    auto copy_a = [&](int p, int hh, int q) __attribute__((always_inline)) {
-        if (q >= P::kCopiesA) return;
+    // Copy q (< 8) of A pair p (group 1): half q / kCopiesA, copy q % kCopiesA
+    // of that half; the 128-row tile has four copies per pair (q >= 4 issues
+    // nothing).
+    auto copy_a = [&](int p, int q) __attribute__((always_inline)) {
+        if (q >= 2 * P::kCopiesA) return;
+        const int hh = q / P::kCopiesA, qq = q % P::kCopiesA;
         const int k0 = 2 * kBK * p;
-        const uint32_t off = (8 * a_chunk < K - k0) ? (hh ? voff1[q] : voff0[q]) : kOutOfRange;
-        const uint32_t st = lds0 + (p % kStagesA) * kStageABytes + (kHalf * hh + 8 * (4 * q + wl)) * 128;
+        const uint32_t off = (8 * a_chunk < K - k0) ? (hh ? voff1[qq] : voff0[qq]) : kOutOfRange;
+        const uint32_t st = lds0 + (p % kStagesA) * kStageABytes + (kHalf * hh + 8 * (4 * qq + wl)) * 128;
         load_to_lds<16>(ra, st, off, static_cast<uint32_t>(k0) * 2);
     };
     // Copy q of B slab m (group 0); rb is the B resource rebased to the slab.
@@ -185,10 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         }
     }
 
-    // Part p of the fragments of slab s, into register set d: B block p (two
-    // transposed reads) and A blocks p kMB/4 .. (p+1) kMB/4 - 1 (two, or one
-    // for 128 rows). Deep intervals hold a pair of slabs in sets 0 and 1.
-    bf16x8 fa[DEPTH][kMB], fb[DEPTH][kNB];
+    // Part p of the fragments of slab s, into register set d (slab s%2 of a
+    // pair): B block p (two transposed reads) and A blocks p kMB/4 ..
+    // (p+1) kMB/4 - 1 (two, or one for 128 rows).
+    bf16x8 fa[2][kMB], fb[2][kNB];
     auto read_part = [&](int s, int p, int d) __attribute__((always_inline)) {
         const uint16_t *sa = lds + ((s >> 1) % kStagesA) * (kStageABytes / 2) + ((s & 1) ? a_off1 : a_off0);
         const uint16_t *sb = lds + (s % kStagesB) * (kStageBBytes / 2);
@@ -201,42 +191,15 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         for (int i = p * kMB / kNB; i < (p + 1) * kMB / kNB; ++i)
             fa[d][i] = *reinterpret_cast<const bf16x8 *>(sa + i * 16 * 64);
     };
-    // The memory role of one interval: read the fragments of slab `rd` (if
-    // `do_read`) and issue this wave's four copies, copy(q). ORDER picks the
-    // instruction order: 0 all reads then all copies, 1 all copies then all
-    // reads, 2 copy/read-part pairs, 3 read-part/copy pairs. (Copies are
-    // volatile asm with a memory clobber, so the order is kept.)
-    auto mem_work = [&](int rd, bool do_read, auto &&copy) __attribute__((always_inline)) {
-        if constexpr (ORDER == 4) {
-            (void)copy;
-            if (do_read)
-#pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
-        } else if constexpr (ORDER == 0 || ORDER == 1) {
-            if (ORDER == 0 && do_read)
-#pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
-#pragma unroll
-            for (int q = 0; q < kCopies; ++q) copy(q);
-            if (ORDER == 1 && do_read)
-#pragma unroll
-                for (int p = 0; p < kNB; ++p) read_part(rd, p, 0);
-        } else {
-            static_assert(kNB == kCopies, "one copy per fragment part");
-#pragma unroll
-            for (int p = 0; p < kNB; ++p) {
-                if (ORDER == 2) copy(p);
-                if (do_read) read_part(rd, p, 0);
-                if (ORDER == 3) copy(p);
-            }
-        }
-    };
-    // The memory role of a deep interval: read both slabs of pair pp (if
-    // `do_read`) and issue this wave's eight copies, copy(q) before part q.
-    // The wave raises its issue priority meanwhile, so that its reads and
-    // copies go out ahead of the MFMA wave on the same SIMD, whose matrix
-    // core has queued work anyway (8192^3: 747 against 754 us; priority 3
-    // gives 749, and raising the MFMA wave instead is slower).
+    // The memory role of one interval: read both slabs of pair pp (if
+    // `do_read`) and issue this wave's eight copies, copy(q) before part q
+    // (issuing all reads first left the texture unit idle while the LDS
+    // worked, and the other way round). The wave raises its issue priority
+    // meanwhile, so that its reads and copies go out ahead of the MFMA wave
+    // on the same SIMD, whose matrix core has queued work anyway (8192^3:
+    // 747 against 754 us; priority 3 gives 749, and raising the MFMA wave
+    // instead is slower). Copies are volatile asm with a memory clobber, so
+    // the order is kept.
     auto mem_work_pair = [&](int pp, bool do_read, auto &&copy) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -254,28 +217,13 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto mfmas = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d)
+        for (int d = 0; d < 2; ++d)
 #pragma unroll
             for (int i = 0; i < kMB; ++i)
 #pragma unroll
                 for (int j = 0; j < kNB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[d][j], fa[d][i], acc[i][j], 0, 0, 0);
     };
-    // ORDER 4: the MFMA role issues the copies, one after every 8 MFMAs.
-    auto mfmas_copy = [&](auto &&copy) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-#pragma unroll
-            for (int j = 0; j < kNB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
-            if (i & 1) {
-                __builtin_amdgcn_sched_barrier(0);
-                copy(i >> 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    };
-    auto no_copy = [](int) {};
     // End of an interval: wait until at most `in_flight` of this wave's
     // copies are outstanding (if in_flight >= 0), then the barrier. The
     // fences keep each interval's work between its barriers (MFMAs touch no
@@ -291,115 +239,49 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
 
     // Each group runs its own loop (one copy of the fragment registers and
     // the MFMA chain per code path); both execute the same barriers.
-    const int nk = (K + kBK - 1) / kBK;
-    if constexpr (DEPTH == 2) {
-        const int np = (K + 2 * kBK - 1) / (2 * kBK);
-        // Copy q (< 8) of A pair p (group 1): half q / kCopiesA; the 128-row
-        // tile has four copies per pair (q >= 4 issues nothing).
-        auto copy_a_pair = [&](int p, int q) __attribute__((always_inline)) {
-            if (q < 2 * P::kCopiesA) copy_a(p, q / P::kCopiesA, q % P::kCopiesA);
-        };
-        if (np > 0) {
-            if (grp == 1) {
-#pragma unroll
-                for (int p = 0; p < 2; ++p)
-#pragma unroll
-                    for (int q = 0; q < 2 * kNB; ++q) copy_a_pair(p, q);
-            } else {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const rsrc_t rb = b_rsrc(m);
-#pragma unroll
-                    for (int q = 0; q < kCopiesB; ++q) copy_b(m, q, rb);
-                }
-            }
-            interval_end(grp == 1 ? 2 * P::kCopiesA : 0);   // pair 0 has landed
-            if (grp == 0) {
-                {
-                    const rsrc_t rb0 = b_rsrc(2), rb1 = b_rsrc(3);
-                    mem_work_pair(0, true, [&](int q) __attribute__((always_inline)) {
-                        copy_b(2 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
-                    });                                               // J_-1
-                }
-                interval_end(-1);
-                for (int p = 0; p < np; ++p) {
-                    mfmas();                                          // J_2p
-                    interval_end(0);                                  // B pair p+1 has landed
-                    const rsrc_t rb0 = b_rsrc(2 * p + 4), rb1 = b_rsrc(2 * p + 5);
-                    auto copy_b_pair = [&](int q) __attribute__((always_inline)) {
-                        copy_b(2 * p + 4 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
-                    };
-                    // J_2p+1. The last pair has nothing left to read; one
-                    // branch here, not one per fragment part (1.5% faster at
-                    // 8192^3).
-                    if (p + 1 < np) mem_work_pair(p + 1, true, copy_b_pair);
-                    else mem_work_pair(p + 1, false, copy_b_pair);
-                    interval_end(-1);
-                }
-            } else {
-                interval_end(-1);                                     // J_-1
-                for (int p = 0; p < np; ++p) {
-                    mem_work_pair(p, true, [&](int q) __attribute__((always_inline)) { copy_a_pair(p + 2, q); });
-                    interval_end(2 * P::kCopiesA);                    // A pair p+1 has landed
-                    mfmas();                                          // J_2p+1
-                    interval_end(-1);
-                }
-            }
-        }
-    } else if (nk > 0) {
+    const int np = (K + 2 * kBK - 1) / (2 * kBK);
+    if (np > 0) {
         if (grp == 1) {
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int q = 0; q < kCopies; ++q) copy_a(p, hh, q);
+                for (int q = 0; q < 2 * kNB; ++q) copy_a(p, q);
         } else {
 #pragma unroll
-            for (int m = 0; m < 3; ++m) {
+            for (int m = 0; m < 2; ++m) {
                 const rsrc_t rb = b_rsrc(m);
 #pragma unroll
-                for (int q = 0; q < kCopies; ++q) copy_b(m, q, rb);
+                for (int q = 0; q < kCopiesB; ++q) copy_b(m, q, rb);
             }
         }
-        interval_end(grp == 1 ? 2 * P::kCopiesA : 2 * kCopiesB);   // slab 0 has landed
+        interval_end(grp == 1 ? 2 * P::kCopiesA : 0);   // pair 0 has landed
         if (grp == 0) {
-            if constexpr (ORDER == 4) {
-                mem_work(0, true, no_copy);          // I_-1
-            } else {
-                const rsrc_t rb = b_rsrc(3);
-                mem_work(0, true, [&](int q) __attribute__((always_inline)) { copy_b(3, q, rb); });   // I_-1
+            {
+                const rsrc_t rb0 = b_rsrc(2), rb1 = b_rsrc(3);
+                mem_work_pair(0, true, [&](int q) __attribute__((always_inline)) {
+                    copy_b(2 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
+                });                                               // J_-1
             }
             interval_end(-1);
-            for (int k = 0; k < nk; ++k) {
-                if constexpr (ORDER == 4) {          // I_2k (B slab k+3 replaces slab k-1)
-                    const rsrc_t rb = b_rsrc(k + 3);
-                    mfmas_copy([&](int q) __attribute__((always_inline)) { copy_b(k + 3, q, rb); });
-                } else {
-                    mfmas();                         // I_2k
-                }
-                interval_end(2 * kCopiesB);          // slab k+1 has landed
-                if constexpr (ORDER == 4) {          // I_2k+1
-                    mem_work(k + 1, k + 1 < nk, no_copy);
-                } else {
-                    const rsrc_t rb = b_rsrc(k + 4);
-                    mem_work(k + 1, k + 1 < nk, [&](int q) __attribute__((always_inline)) { copy_b(k + 4, q, rb); });
-                }
+            for (int p = 0; p < np; ++p) {
+                mfmas();                                          // J_2p
+                interval_end(0);                                  // B pair p+1 has landed
+                const rsrc_t rb0 = b_rsrc(2 * p + 4), rb1 = b_rsrc(2 * p + 5);
+                auto copy_b_pair = [&](int q) __attribute__((always_inline)) {
+                    copy_b(2 * p + 4 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
+                };
+                // J_2p+1. The last pair has nothing left to read; one branch
+                // here, not one per fragment part (1.5% faster at 8192^3).
+                if (p + 1 < np) mem_work_pair(p + 1, true, copy_b_pair);
+                else mem_work_pair(p + 1, false, copy_b_pair);
                 interval_end(-1);
             }
         } else {
-            interval_end(-1);                        // I_-1
-            for (int k = 0; k < nk; ++k) {
-                const int p = (k + 4) >> 1, hh = k & 1;
-                if constexpr (ORDER == 4) {
-                    mem_work(k, true, no_copy);      // I_2k
-                    interval_end(4);                 // slab k+1 has landed
-                    mfmas_copy([&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k+1
-                } else {
-                    mem_work(k, true, [&](int q) __attribute__((always_inline)) { copy_a(p, hh, q); });   // I_2k
-                    interval_end(2 * P::kCopiesA);   // slab k+1 has landed
-                    mfmas();                         // I_2k+1
-                }
+            interval_end(-1);                                     // J_-1
+            for (int p = 0; p < np; ++p) {
+                mem_work_pair(p, true, [&](int q) __attribute__((always_inline)) { copy_a(p + 2, q); });
+                interval_end(2 * P::kCopiesA);                    // A pair p+1 has landed
+                mfmas();                                          // J_2p+1
                 interval_end(-1);
             }
         }
@@ -445,53 +327,39 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
     });
 }
 
-template <int BM, int ORDER, int GROUP_M, int DEPTH>
+// Tile-row bands of this height are walked column by column inside each XCD's
+// range of tiles (tile_of); 4 and 8 tie at 8192^3, 2, 16 and 32 are slower.
+constexpr int kGroupM = 8;
+
+template <int BM>
 hipError_t launch_pingpong(const Problem &p, int64_t grid, hipStream_t stream)
 {
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((mmrelu_bf16_pingpong<BM, ORDER, DEPTH>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((mmrelu_bf16_pingpong<BM>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
-                       static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, GROUP_M,
+                       static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, kGroupM,
                        static_cast<const uint16_t *>(p.bias), p.act);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// 256 x 256 tiles: the planner's bf16 tile kernel for large aligned products
+// (8192^3: 753 us against 804 for a schedule with one slab per interval).
 const Variant *variant_bf16_pingpong256()
 {
-    static const Variant v = {"mmrelu_bf16_pingpong<256,256,32,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 32, 512, 1, 8,
-                              launch_pingpong<256, 2, 8, 1>};
+    static const Variant v = {"mmrelu_bf16_pingpong<256,256,64,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 64, 512, 1, 8,
+                              launch_pingpong<256>};
     return &v;
 }
 // 128 x 256 tiles: twice the tiles of the 256 x 256 grid, for products that
-// would leave CUs idle on it. Relative cost per output 1.32 (8192^3: 1085
-// against 823 us); measured wins: 1024 x 8192 x 8192, 155 us against 175 on
-// 256 x 256 tiles and 179 on 128 x 128; 2048 x 4096 x 4096, 91 against 97.
+// would leave CUs idle on it. Relative cost per output 1.33: one 128 x 256
+// tile of K = 8192 per CU takes 126 us (1024 x 8192 x 8192), a 256 x 256 tile
+// 188 us (a quarter of 8192^3).
 const Variant *variant_bf16_pingpong128()
 {
-    static const Variant v = {"mmrelu_bf16_pingpong<128,256,32,A3B4>", MMRELU_DTYPE_BF16, 128, 256, 32, 512, 1, 8,
-                              launch_pingpong<128, 2, 8, 1>, 1.32f};
-    return &v;
-}
-
-// Deep intervals (64 k per interval, one barrier per 64 k) on the same tiles:
-// the planner's bf16 tile kernels. Measured against the 32-deep schedule on
-// one box: 8192^3, 753 against 804 us (N(0,1)/sqrt(K) inputs) and 578
-// against 630 (zeros); 4096^3, 104 against 110; 1024 x 8192 x 8192 on the
-// 128-row tile, 126 against 137.
-const Variant *variant_bf16_pingpong256_deep()
-{
-    static const Variant v = {"mmrelu_bf16_pingpong<256,256,64,A3B4>", MMRELU_DTYPE_BF16, 256, 256, 64, 512, 1, 8,
-                              launch_pingpong<256, 2, 8, 2>};
-    return &v;
-}
-// Relative cost per output 1.33: one 128 x 256 tile of K = 8192 per CU takes
-// 126 us (1024 x 8192 x 8192), a 256 x 256 tile 188 us (a quarter of 8192^3).
-const Variant *variant_bf16_pingpong128_deep()
-{
     static const Variant v = {"mmrelu_bf16_pingpong<128,256,64,A3B4>", MMRELU_DTYPE_BF16, 128, 256, 64, 512, 1, 8,
-                              launch_pingpong<128, 2, 8, 2>, 1.33f};
+                              launch_pingpong<128>, 1.33f};
     return &v;
 }
 

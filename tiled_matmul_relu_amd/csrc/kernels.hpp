@@ -43,13 +43,9 @@ const Variant *variant_f32_mfma128();
 const Variant *variant_f32_mfma128_unaligned();
 const Variant *variant_f32_mfma64();
 const Variant *variant_f32_mfma64_unaligned();
-const Variant *variant_bf16_mfma256();
-const Variant *variant_bf16_mfma256_8w();
-const Variant *variant_bf16_pingpong256();
+const Variant *variant_bf16_pingpong256();   // k_bf16_pingpong.hip
 const Variant *variant_bf16_pingpong128();
-const Variant *variant_bf16_pingpong256_deep();
-const Variant *variant_bf16_pingpong128_deep();
-const Variant *variant_bf16_mfma128();
+const Variant *variant_bf16_mfma128();       // k_bf16_mfma.hip
 // Skinny kernels (k_skinny.hip), tiles of 16 mb x 16 nb with K split over
 // the eight waves and ks k blocks per slab: (mb, nb, ks) = (1, 2, 1),
 // (2, 2, 1), (4, 2, 2 for fp32 / 1 for bf16) for skinny M, (2, 1, 2),

@@ -16,7 +16,10 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 15;
-constexpr int kNumBf16 = 19;
+constexpr int kNumBf16 = 15;
+// Both tables: 0 the plain kernel; 1 the large aligned tile and 2 the large
+// tile for any layout; 3 and 4 smaller tiles; 5 - 10 and 12 the skinny
+// tiles; 11 the matrix-vector kernel; 13 and 14 the rest.
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -31,16 +34,14 @@ const Variant *const *f32_table()
 }
 const Variant *const *bf16_table()
 {
-    static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_mfma256(),
-                                               variant_bf16_mfma256_8w(), variant_bf16_pingpong256(),
+    static const Variant *const t[kNumBf16] = {variant_bf16_simple(), variant_bf16_pingpong256(),
+                                               variant_bf16_any(128), variant_bf16_pingpong128(),
                                                variant_bf16_mfma128(), variant_bf16_skinny(1, 2, 1),
                                                variant_bf16_skinny(2, 2, 1), variant_bf16_skinny(4, 2, 1),
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
-                                               variant_bf16_any(128), variant_bf16_skinny(1, 4, 1),
-                                               variant_bf16_pingpong128(), variant_bf16_pingpong256_deep(),
-                                               variant_bf16_pingpong128_deep()};
+                                               variant_bf16_skinny(1, 4, 1)};
     return t;
 }
 
@@ -113,18 +114,18 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
 // full tiles of block_m x block_n outputs at the variant's measured relative
 // cost per output (wave quantisation of the grid over the CUs). bf16
 // layouts the 16-byte-vector kernels do not accept go to the any-layout
-// matrix-core kernel (variants 13 and 14); the plain tiled kernel (variant 0) is
+// matrix-core kernel (variants 2 and 13); the plain tiled kernel (variant 0) is
 // only reached through the _variant entry points.
 // Pointers are taken as 16-byte aligned when null (planning without buffers).
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                        const void *A, const void *B, const void *C, int32_t cus)
 {
-    static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {17, 4};
+    static const int32_t f32_aligned[] = {1, 3}, f32_any[] = {2, 4}, bf16_aligned[] = {1, 4};
     const Variant *const *table = dtype == MMRELU_DTYPE_F32 ? f32_table() : bf16_table();
     // A single output column is a matrix-vector product: one read of A, one
     // wave per output (variant 11), whatever the layout.
     if (N == 1) return 11;
-    const bool fits = layout_fits(table[dtype == MMRELU_DTYPE_F32 ? 1 : 3], N, K, lda, ldb, ldc, A, B, C);
+    const bool fits = layout_fits(table[1], N, K, lda, ldb, ldc, A, B, C);
     // Skinny M or N (<= 64): the product is bound by reading the large
     // operand once, and the skinny kernels spread that read over one
     // workgroup per 32 columns of B (skinny M: variants 5, 6, 7 for up to 16,
@@ -132,13 +133,13 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     // 16, 32, 64 columns), with K split across eight waves. When both are
     // small, the smaller one decides.
     // At most 16 rows and a 64-column strip for every CU: 64-column strips
-    // (fp32 variant 13, bf16 variant 15), which read whole lines of B per
+    // (fp32 variant 13, bf16 variant 14), which read whole lines of B per
     // row (bf16) and keep the strip count at or under twice the CUs.
     if (fits && (M <= 64 || N <= 64)) {
         int32_t v;
         if (M <= 64 && M <= N) v = M <= 16 ? 5 : M <= 32 ? 6 : 7;
         else v = N <= 16 ? 8 : N <= 32 ? 9 : 10;
-        if (v == 5 && (N + 63) / 64 >= cus) v = dtype == MMRELU_DTYPE_BF16 ? 15 : 13;
+        if (v == 5 && (N + 63) / 64 >= cus) v = dtype == MMRELU_DTYPE_BF16 ? 14 : 13;
         // fp32, at most 16 columns and a 64-row band for every CU: 64-row
         // bands (variant 14).
         if (v == 8 && dtype == MMRELU_DTYPE_F32 && (M + 63) / 64 >= cus) v = 14;
@@ -148,12 +149,12 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     if (dtype == MMRELU_DTYPE_F32) cand = fits ? f32_aligned : f32_any;
     else if (fits) cand = bf16_aligned;
     else {
-        // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 14)
+        // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 2)
         // once their grid gives every CU one or more, else 64 x 64 tiles
         // (variant 13), which keep more CUs busy (measured: 2047^3, 64.5
         // against 76.7 us; 1001^3, 33.6 against 21.1 us).
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        return tiles128 >= static_cast<int64_t>(cus) ? 14 : 13;
+        return tiles128 >= static_cast<int64_t>(cus) ? 2 : 13;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
     // seven skinny tiles (variants 5 - 10 and 12), which split K over eight
@@ -178,7 +179,7 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     };
     consider(cand[0], true);
     consider(cand[1], true);
-    if (fits && dtype == MMRELU_DTYPE_BF16) consider(18, true);   // the 128 x 256 ping-pong tile
+    if (fits && dtype == MMRELU_DTYPE_BF16) consider(3, true);    // the 128 x 256 ping-pong tile
     if (fits) {
         for (int32_t v = 5; v <= 10; ++v) consider(v, false);
         consider(12, false);
