@@ -10,7 +10,12 @@ Prints one JSON line: throughput (TFLOP/s, 2MNK per step), the roofline
 object for the dominant kernel (achieved FLOP/s per launch from HIP events on
 the launch stream against the bf16 dense matrix-core peak) and the CPU
 baseline (the fp64 oracle timed on a bounded sample of the same workload on
-this host's cores).
+this host's cores), whose result is compared with the timed output (parity).
+
+Order of the GPU work: the headline's W warm-up and K timed calls run twice
+in a row, first as `cold_start` (the board's power management settles over
+the first ~25 calls of a process), then for `value`; then the matrix-core
+ceiling probe, the all-zero power check and the fp32 workload.
 """
 import argparse
 import dataclasses
@@ -159,12 +164,9 @@ def to_device(x, torch):
     return torch.from_numpy(x).cuda()
 
 
-def time_workload(cfg, steps, warmup, torch, mm, datagen):
-    """W warm-up calls, then `steps` calls back to back between two HIP events
-    on the launch stream (the timed region: ms per call = elapsed / steps),
-    then `steps` more calls with an event after each, for the distribution
-    of single calls (mean, median, P95). Returns the times, the plan, the
-    host inputs and the device output of the last call."""
+def prepare_workload(cfg, torch, mm, datagen):
+    """Host inputs of a workload, their device copies, a NaN-filled C and the
+    call's arguments on torch's current stream."""
     a, b = datagen.make_inputs(cfg)
     da, db = to_device(a, torch), to_device(b, torch)
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
@@ -173,6 +175,18 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     fn = mm.mmrelu_f32 if cfg.dtype == "f32" else mm.mmrelu_bf16
     args = (da.data_ptr(), db.data_ptr(), c.data_ptr(), cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc,
             stream.cuda_stream)
+    plan = mm.mmrelu_plan(mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16, cfg.M, cfg.N, cfg.K,
+                          cfg.lda, cfg.ldb, cfg.ldc)
+    return {"cfg": cfg, "fn": fn, "args": args, "stream": stream, "plan": plan, "inputs": (a, b),
+            "da": da, "db": db, "c": c}
+
+
+def time_calls(w, steps, warmup, torch, mm):
+    """W warm-up calls, then `steps` calls back to back between two HIP events
+    on the launch stream (the timed region: ms per call = elapsed / steps),
+    then `steps` more calls with an event after each, for the distribution
+    of single calls (mean, median, P95)."""
+    cfg, fn, args, stream = w["cfg"], w["fn"], w["args"], w["stream"]
     for _ in range(warmup):
         rc = fn(*args)
         if rc != mm.MMRELU_OK:
@@ -196,10 +210,13 @@ def time_workload(cfg, steps, warmup, torch, mm, datagen):
     per_call = {"calls": steps, "mean_ms": round(sum(t) / steps, 4), "median_ms": round(median(t), 4),
                 "p95_ms": round(t[min(steps - 1, int(math.ceil(0.95 * steps)) - 1)], 4),
                 "tflops_median": round(cfg.flops / (median(t) * 1e-3) / 1e12, 2)}
-    plan = mm.mmrelu_plan(mm.DTYPE_F32 if cfg.dtype == "f32" else mm.DTYPE_BF16, cfg.M, cfg.N, cfg.K,
-                          cfg.lda, cfg.ldb, cfg.ldc)
-    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "per_call": per_call, "plan": plan,
-            "inputs": (a, b), "da": da, "db": db, "c": c}
+    return {"ms": ms, "tflops": cfg.flops / (ms * 1e-3) / 1e12, "per_call": per_call}
+
+
+def time_workload(cfg, steps, warmup, torch, mm, datagen):
+    """prepare_workload, then time_calls; returns both records merged."""
+    w = prepare_workload(cfg, torch, mm, datagen)
+    return {**w, **time_calls(w, steps, warmup, torch, mm)}
 
 
 def median(sorted_t):
@@ -673,7 +690,16 @@ def main():
     mm.load_library()
 
     head = datagen.CONFIGS[5]
-    res = time_workload(head, args.steps, args.warmup, torch, mm, datagen)
+    res = prepare_workload(head, torch, mm, datagen)
+    # The first calls of a process run while the board's power management
+    # settles: after a few fast calls it cuts the clock hard and then
+    # releases it over ~25 calls of this kernel (per-call trace 750, 745,
+    # 812, 941, 1040, 984, 913, ... 760, 748 us). The same W + K calls are
+    # therefore run and timed twice, back to back: first at the process's
+    # cold start (reported as cold_start), then again for `value`, the
+    # steady state that a job issuing this call repeatedly runs in.
+    cold = time_calls(res, args.steps, args.warmup, torch, mm)
+    res.update(time_calls(res, args.steps, args.warmup, torch, mm))
     kernel = res["plan"]["name"]
     achieved = res["tflops"]
     traffic = measured_traffic("bf16", kernel)
@@ -695,11 +721,24 @@ def main():
                    "kernel": kernel, "grid": res["plan"]["grid"]},
         "pct_of_peak": round(100 * achieved / PEAK_TFLOPS["bf16"], 2),
         "per_call": res["per_call"],
+        "cold_start": {"what": "the same W warm-up and K timed calls at the start of the process, timed the same "
+                               "way, before the ones above",
+                       "ms_per_step": round(cold["ms"], 4), "value": round(cold["tflops"], 2), "unit": "TFLOP/s",
+                       "frac": round(cold["tflops"] / PEAK_TFLOPS["bf16"], 4), "per_call": cold["per_call"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": traffic},
     }
     if not args.no_power_check:
+        # The matrix cores alone on the same operand values: the most any
+        # kernel of this product can reach on these inputs under the power
+        # cap. Run right after the product, whose power draw it matches, so
+        # that it starts in the same settled state.
+        mc = mfma_ceiling(res["da"], res["db"], args.steps, args.warmup, torch)
+        out["mfma_ceiling"] = {"what": "bf16 MFMAs alone (no memory traffic), the product's per-wave MFMA "
+                                       "block on operands loaded from A and B; TFLOP/s per MFMA shape",
+                               "unit": "TFLOP/s", **mc,
+                               "value_frac_of_ceiling": round(achieved / mc["workload_16x16"], 4)}
         # Same kernel, same shape, all-zero inputs: the matrix cores see no
         # operand toggling, so the board's power cap does not lower the clock.
         # The gap to `value` is the power cost of random operands, not schedule.
@@ -708,13 +747,7 @@ def main():
         out["power_check"] = {"inputs": "all-zero bf16 A and B, same shape, kernel and launch",
                               "value": round(rz["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(rz["ms"], 4),
                               "frac": round(rz["tflops"] / PEAK_TFLOPS["bf16"], 4)}
-        # The matrix cores alone on the same operand values: the most any
-        # kernel of this product can reach on these inputs under the power cap.
-        mc = mfma_ceiling(res["da"], res["db"], args.steps, args.warmup, torch)
-        out["mfma_ceiling"] = {"what": "bf16 MFMAs alone (no memory traffic), the product's per-wave MFMA "
-                                       "block on operands loaded from A and B; TFLOP/s per MFMA shape",
-                               "unit": "TFLOP/s", **mc,
-                               "value_frac_of_ceiling": round(achieved / mc["workload_16x16"], 4)}
+        del rz
     r32 = None
     if not args.no_f32:
         f = datagen.CONFIGS[3]
