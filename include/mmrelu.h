@@ -71,7 +71,8 @@ enum {
     MMRELU_ERR_INVALID_VALUE = 1,
     MMRELU_ERR_NULL_POINTER = 2,
     MMRELU_ERR_MISALIGNED = 3,
-    MMRELU_ERR_LAUNCH = 4
+    MMRELU_ERR_LAUNCH = 4,
+    MMRELU_ERR_WORKSPACE_LIMIT = 5   /* mmrelu_strided_static only */
 };
 
 enum { MMRELU_DTYPE_F32 = 0, MMRELU_DTYPE_BF16 = 1 };
@@ -166,6 +167,32 @@ int mmrelu_strided_f32(int act, const float *A, const float *B, const float *bia
 int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uint16_t *bias, uint16_t *C,
                         int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
                         int64_t scm, int64_t scn, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The general-stride call without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, semantics and checks as
+ * mmrelu_strided_f32 / _bf16 (dtype MMRELU_DTYPE_F32 or MMRELU_DTYPE_BF16
+ * selects which; A, B, bias and C point to elements of that type), but the
+ * operand copies and the row-major temporary of C go to a fixed device array
+ * of MMRELU_STATIC_WORKSPACE_BYTES that the library holds on each device it
+ * runs on, from that device's first such call until the process ends.
+ * Nothing is allocated or freed and nothing is cleared (every byte the
+ * kernels read from the array was written earlier in the same call).
+ *   - A call whose mmrelu_strided_workspace_size exceeds the limit returns
+ *     MMRELU_ERR_WORKSPACE_LIMIT before anything is enqueued; calls that
+ *     need no workspace (row-major or in-place layouts) never touch it.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents: calls that may overlap on one device (different
+ *     streams, or host threads without ordering) race and must not be mixed;
+ *     calls ordered on one stream are safe.
+ *   - MMRELU_ERR_LAUNCH if the device address of the array cannot be
+ *     obtained (hipGetSymbolAddress, once per device), or a launch fails.
+ */
+#define MMRELU_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int mmrelu_strided_static(int dtype, int act, const void *A, const void *B, const void *bias, void *C,
+                          int64_t M, int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn,
+                          int64_t scm, int64_t scn, void *stream);
 
 /*
  * Row softmax and row sum: the two rungs before the matmul on the lecture's

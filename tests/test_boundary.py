@@ -366,6 +366,36 @@ def test_strided_entry_points_check_workspace_before_launch():
     assert mm.mmrelu_strided_f32(mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 0, N, K, 1, 1, 1, 1, 1, 1, 0, 0) == mm.MMRELU_OK
 
 
+def test_strided_static_checks_before_any_hip_call():
+    """mmrelu_strided_static validates like the strided entry points and
+    refuses a call needing more than its fixed workspace before anything
+    touches the device (these stand-in pointers are never dereferenced)."""
+    M = N = K = 8192
+    need = _ws(mm.DTYPE_BF16, M, N, K, 1, M, N, 1, N, 1)            # A^T: 128 MiB
+    assert need == M * K * 2 > mm.STATIC_WORKSPACE_BYTES
+    st = mm.mmrelu_strided_static
+    assert st(mm.DTYPE_BF16, mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, M, N, K, 1, M, N, 1, N, 1) == \
+        mm.MMRELU_ERR_WORKSPACE_LIMIT
+    assert "MMRELU_STATIC_WORKSPACE_BYTES" in mm.status_string(mm.MMRELU_ERR_WORKSPACE_LIMIT)
+    # just under the limit is planned, just over is refused: 4096 x 4096 bf16 A^T is 32 MiB
+    assert _ws(mm.DTYPE_BF16, 4096, 4096, 4096, 1, 4096, 4096, 1, 4096, 1) <= mm.STATIC_WORKSPACE_BYTES
+    assert _ws(mm.DTYPE_F32, 4096, 4096, 4096, 1, 4096, 1, 4096, 4096, 1) > mm.STATIC_WORKSPACE_BYTES
+    assert st(mm.DTYPE_F32, mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 4096, 4096, 4096, 1, 4096, 1, 4096, 4096, 1) == \
+        mm.MMRELU_ERR_WORKSPACE_LIMIT
+    # the strided entry points' own checks come first
+    assert st(7, mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 64, 32, 16, 16, 1, 32, 1, 32, 1) == mm.MMRELU_ERR_INVALID_VALUE
+    assert st(mm.DTYPE_F32, 9, _P, 2 * _P, 0, 3 * _P, 64, 32, 16, 16, 1, 32, 1, 32, 1) == \
+        mm.MMRELU_ERR_INVALID_VALUE
+    assert st(mm.DTYPE_F32, mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 64, 32, 16, 16, 1, 32, 1, 1, 1) == \
+        mm.MMRELU_ERR_INVALID_VALUE
+    assert st(mm.DTYPE_F32, mm.ACT_RELU, _P + 2, 2 * _P, 0, 3 * _P, 64, 32, 16, 16, 1, 32, 1, 32, 1) == \
+        mm.MMRELU_ERR_MISALIGNED
+    assert st(mm.DTYPE_F32, mm.ACT_RELU, _P, 2 * _P, 0, 0, 64, 32, 16, 16, 1, 32, 1, 32, 1) == \
+        mm.MMRELU_ERR_NULL_POINTER
+    # empty outputs: nothing to do
+    assert st(mm.DTYPE_F32, mm.ACT_RELU, _P, 2 * _P, 0, 3 * _P, 0, 32, 16, 1, 1, 1, 1, 1, 1) == mm.MMRELU_OK
+
+
 # --- row softmax and row sum: validation and kernel choice (no launch) -------
 
 def test_softmax_variant_choice():

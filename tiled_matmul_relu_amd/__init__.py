@@ -25,6 +25,8 @@ MMRELU_ERR_INVALID_VALUE = 1
 MMRELU_ERR_NULL_POINTER = 2
 MMRELU_ERR_MISALIGNED = 3
 MMRELU_ERR_LAUNCH = 4
+MMRELU_ERR_WORKSPACE_LIMIT = 5
+STATIC_WORKSPACE_BYTES = 64 << 20
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 ACT_RELU = 0
@@ -37,7 +39,7 @@ EXPORTED = (
     "mmrelu_plan", "mmrelu_num_variants", "mmrelu_plan_variant",
     "mmrelu_wave_quantization", "mmrelu_f32_variant", "mmrelu_bf16_variant",
     "mmrelu_fused_f32", "mmrelu_fused_bf16", "mmrelu_fused_f32_variant", "mmrelu_fused_bf16_variant",
-    "mmrelu_strided_workspace_size", "mmrelu_strided_f32", "mmrelu_strided_bf16",
+    "mmrelu_strided_workspace_size", "mmrelu_strided_f32", "mmrelu_strided_bf16", "mmrelu_strided_static",
     "mmrelu_softmax_rows_f32", "mmrelu_softmax_rows_bf16", "mmrelu_softmax_rows_f32_variant",
     "mmrelu_softmax_rows_bf16_variant", "mmrelu_softmax_rows_variant", "mmrelu_row_sum_f32", "mmrelu_row_sum_bf16",
 )
@@ -98,6 +100,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         fn.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, vp,
                        ctypes.c_size_t, vp]
         fn.restype = ctypes.c_int
+    lib.mmrelu_strided_static.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                          i64, i64, i64, vp]
+    lib.mmrelu_strided_static.restype = ctypes.c_int
     lib.mmrelu_strided_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64,
                                                   i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.mmrelu_strided_workspace_size.restype = ctypes.c_int
@@ -216,6 +221,15 @@ def mmrelu_strided_bf16(act: int, A: int, B: int, bias: int, C: int, M: int, N: 
     """Enqueue C = act(A·B + bias), bf16 in/out, with an element stride per dimension of A, B and C."""
     return load_library().mmrelu_strided_bf16(act, A, B, bias or None, C, M, N, K, sam, sak, sbk, sbn, scm, scn,
                                               workspace or None, workspace_bytes, stream)
+
+
+def mmrelu_strided_static(dtype: int, act: int, A: int, B: int, bias: int, C: int, M: int, N: int, K: int,
+                          sam: int, sak: int, sbk: int, sbn: int, scm: int, scn: int, stream: int = 0) -> int:
+    """Enqueue the general-stride call of `dtype` with its workspace taken
+    from the library's fixed device array (no allocation); returns the
+    status (MMRELU_ERR_WORKSPACE_LIMIT past STATIC_WORKSPACE_BYTES)."""
+    return load_library().mmrelu_strided_static(dtype, act, A, B, bias or None, C, M, N, K, sam, sak, sbk, sbn,
+                                                scm, scn, stream)
 
 
 def mmrelu_softmax_rows_f32(X: int, Y: int, M: int, N: int, ldx: int, ldy: int, stream: int = 0) -> int:

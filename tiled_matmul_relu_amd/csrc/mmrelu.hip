@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mmrelu.h"
 #include "kernels.hpp"
@@ -391,6 +392,43 @@ int run_strided(int dtype, int act, const void *A, const void *B, const void *bi
     return MMRELU_OK;
 }
 
+// Workspace of mmrelu_strided_static: a fixed array in device memory, one
+// copy per device (created with the library's code object on that device and
+// held until the process ends), so that the call allocates nothing. In host
+// code `scratch` names a host-side stand-in: kernels and copies are given the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticWorkspaceBytes = MMRELU_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_address[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept; null if HIP fails.
+void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void *p = g_scratch_address[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_address[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_address[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
+}
+
 // Row operations: shared argument checks. ld must cover the row and the
 // largest offset must stay below 2^60.
 int check_rows(const void *X, const void *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy, size_t esize_x,
@@ -536,6 +574,23 @@ int mmrelu_strided_bf16(int act, const uint16_t *A, const uint16_t *B, const uin
                        workspace_bytes, stream);
 }
 
+int mmrelu_strided_static(int dtype, int act, const void *A, const void *B, const void *bias, void *C, int64_t M,
+                          int64_t N, int64_t K, int64_t sam, int64_t sak, int64_t sbk, int64_t sbn, int64_t scm,
+                          int64_t scn, void *stream)
+{
+    StridedPlan p;
+    const int rc = plan_strided(dtype, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, p);
+    if (rc != MMRELU_OK) return rc;
+    if (p.bytes > kStaticWorkspaceBytes) return MMRELU_ERR_WORKSPACE_LIMIT;
+    void *ws = nullptr;
+    if (p.bytes > 0 && M > 0 && N > 0) {
+        ws = scratch_address();
+        if (ws == nullptr) return MMRELU_ERR_LAUNCH;
+    }
+    return run_strided(dtype, act, A, B, bias, C, M, N, K, sam, sak, sbk, sbn, scm, scn, ws, kStaticWorkspaceBytes,
+                       stream);
+}
+
 int mmrelu_softmax_rows_f32(const float *X, float *Y, int64_t M, int64_t N, int64_t ldx, int64_t ldy, void *stream)
 {
     return softmax_rows(4, -1, X, Y, M, N, ldx, ldy, stream);
@@ -597,6 +652,8 @@ const char *mmrelu_status_string(int status)
     case MMRELU_ERR_NULL_POINTER: return "null pointer";
     case MMRELU_ERR_MISALIGNED: return "pointer not aligned to its element size";
     case MMRELU_ERR_LAUNCH: return "kernel launch failed";
+    case MMRELU_ERR_WORKSPACE_LIMIT:
+        return "the call needs more workspace than the library's fixed buffer (MMRELU_STATIC_WORKSPACE_BYTES) holds";
     default: return "unknown status";
     }
 }
