@@ -52,9 +52,12 @@
 //           of pair p, which group 1 read in J_2p);
 //           group 1 multiplies pair p.
 // A pair p+2's stage last held pair p-1, read by group 1 in J_2p-2.
-// Copies past K are fully masked (they zero-fill stages that are never
-// read), so every interval costs the same vmcnt count and the loop has no
-// data-dependent branches.
+// Copies are issued only for pairs that hold some k < K (the prologue's
+// copies of pair 1 aside); the last pairs are peeled off both loops, so the
+// loops themselves have no branches.
+// End of the tile: group 0's last MFMAs come one interval before group 1's,
+// and group 0 stores its half of the tile in that interval, while group 1
+// runs the tile's last MFMAs; group 1 stores after the last barrier.
 //
 // Requires lda, ldb, ldc, K and N to be multiples of 8 and 16-byte aligned
 // pointers.
@@ -237,8 +240,52 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
+    // and activation on fp32, round to bf16, one 8-byte masked store. The
+    // bias values of the lane's columns are loaded once, up front, and only
+    // when there is a bias; stores go row block by row block, so the four
+    // column blocks of a row complete its lines back to back.
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0,
+                                                          ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * 2);
+        float bj[kNB][4];
+        if (bias != nullptr) {
+            const __amdgpu_buffer_rsrc_t rb = make_bias_rsrc(bias, n0, N, 2);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rb, wn * 64 + j * 16 + 4 * g + r);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
+        }
+        with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+                const int row = wm * kHalf + i * 16 + t;
+#pragma unroll
+                for (int j = 0; j < kNB; ++j) {
+                    const int col = wn * 64 + j * 16 + 4 * g;
+                    const f32x4 v = acc[i][j];
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[j][r]));
+                    const uint32_t off =
+                        (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
+                    store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+                }
+            }
+        });
+    };
+    auto no_copy = [](int) {};
+
     // Each group runs its own loop (one copy of the fragment registers and
-    // the MFMA chain per code path); both execute the same barriers.
+    // the MFMA chain per code path); both execute the same barriers. Copies
+    // are issued only for pairs that hold some k < K; the prologue's copies
+    // of pair 1 are the exception (masked zero fills when K <= 64).
     const int np = (K + 2 * kBK - 1) / (2 * kBK);
     if (np > 0) {
         if (grp == 1) {
@@ -263,68 +310,51 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_pingpong(
                 });                                               // J_-1
             }
             interval_end(-1);
-            for (int p = 0; p < np; ++p) {
+            // J_2p+1 reads pair p+1 and copies B pair p+2 while they exist;
+            // the last two pairs are peeled off the loop, so the loop has no
+            // branch and the fragment registers are dead by the epilogue.
+            int p = 0;
+            for (; p + 2 < np; ++p) {
                 mfmas();                                          // J_2p
                 interval_end(0);                                  // B pair p+1 has landed
                 const rsrc_t rb0 = b_rsrc(2 * p + 4), rb1 = b_rsrc(2 * p + 5);
-                auto copy_b_pair = [&](int q) __attribute__((always_inline)) {
+                mem_work_pair(p + 1, true, [&](int q) __attribute__((always_inline)) {
                     copy_b(2 * p + 4 + q / kCopiesB, q % kCopiesB, q < kCopiesB ? rb0 : rb1);
-                };
-                // J_2p+1. The last pair has nothing left to read; one branch
-                // here, not one per fragment part (1.5% faster at 8192^3).
-                if (p + 1 < np) mem_work_pair(p + 1, true, copy_b_pair);
-                else mem_work_pair(p + 1, false, copy_b_pair);
+                });                                               // J_2p+1
                 interval_end(-1);
             }
+            if (p + 1 < np) {                                     // pair np-2: read the last pair
+                mfmas();
+                interval_end(0);
+                mem_work_pair(p + 1, true, no_copy);
+                interval_end(-1);
+            }
+            // The last pair. Nothing is left to read: this group stores its
+            // half of the tile while group 1 runs the tile's last MFMAs.
+            mfmas();
+            interval_end(0);
+            epilogue();
+            interval_end(-1);
         } else {
             interval_end(-1);                                     // J_-1
-            for (int p = 0; p < np; ++p) {
+            // J_2p reads pair p, copies A pair p+2 while it exists, then waits
+            // for pair p+1 (all but the copies just issued, or all).
+            int p = 0;
+            for (; p + 2 < np; ++p) {
                 mem_work_pair(p, true, [&](int q) __attribute__((always_inline)) { copy_a(p + 2, q); });
-                interval_end(2 * P::kCopiesA);                    // A pair p+1 has landed
+                interval_end(2 * P::kCopiesA);
                 mfmas();                                          // J_2p+1
                 interval_end(-1);
             }
-        }
-    }
-
-    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
-    // and activation on fp32, round to bf16, one 8-byte masked store. The
-    // bias values of the lane's columns are loaded once, up front, and only
-    // when there is a bias; stores go row block by row block, so the four
-    // column blocks of a row complete its lines back to back.
-    const __amdgpu_buffer_rsrc_t rc = make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0,
-                                                      ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * 2);
-    float bj[kNB][4];
-    if (bias != nullptr) {
-        const __amdgpu_buffer_rsrc_t rb = make_bias_rsrc(bias, n0, N, 2);
-#pragma unroll
-        for (int j = 0; j < kNB; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rb, wn * 64 + j * 16 + 4 * g + r);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kNB; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
-    }
-    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
-        constexpr int ACT = decltype(act_c)::value;
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            const int row = wm * kHalf + i * 16 + t;
-#pragma unroll
-            for (int j = 0; j < kNB; ++j) {
-                const int col = wn * 64 + j * 16 + 4 * g;
-                const f32x4 v = acc[i][j];
-                bf16x4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(v[r] + bj[j][r]));
-                const uint32_t off =
-                    (m0 + row < M && n0 + col < N) ? static_cast<uint32_t>((row * ldc + col) * 2) : kOutOfRange;
-                store_b64(rc, off, __builtin_bit_cast(u32x2, o));
+            for (; p < np; ++p) {
+                mem_work_pair(p, true, no_copy);
+                interval_end(0);
+                mfmas();
+                interval_end(-1);
             }
         }
-    });
+    }
+    if (grp == 1 || np == 0) epilogue();
 }
 
 // Tile-row bands of this height are walked column by column inside each XCD's
