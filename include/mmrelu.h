@@ -282,8 +282,11 @@ typedef struct {
  *     K over eight waves and keep every CU busy when the large tiles cannot
  *     (small squares, long K with few output tiles); other layouts run the
  *     fp32 unaligned matrix-core kernels, or for bf16 the any-layout
- *     matrix-core kernel: 128 x 128 tiles (variant 2) when that grid gives
- *     every CU at least one tile, else 64 x 64 tiles (variant 13).
+ *     matrix-core kernels: 64 x 64 tiles (variant 13) until the 128 x 128
+ *     grid gives every CU a tile, then 128 x 128 tiles (variant 2, registers
+ *     realign the operands) or 256 x 256 tiles (variant 15, 4- and 16-byte
+ *     copies to LDS realigned there), whichever finishes its grid in fewer
+ *     estimated rounds (a round of variant 15 counted as 1.6 of variant 2).
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);

@@ -243,12 +243,19 @@ def test_planner_square_skinny_tile():
 
 
 def test_planner_any_layout_tile():
-    """Unaligned bf16: 128x128 tiles once their grid gives every CU one or
-    more, else 64x64 tiles."""
+    """Unaligned bf16: 64x64 tiles until the 128x128 grid gives every CU one
+    or more; then 128x128 tiles (two workgroups a CU) or 256x256 tiles (one),
+    whichever grid takes fewer estimated rounds, a 256x256 round counting
+    1.6."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
-    # 4097 x 3001: 33 * 24 = 792 tiles of 128x128 (>= 256)
-    assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_any<128,128,32>"
-    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
+    # 4097 x 3001: 792 tiles of 128x128 (2 rounds of 512) against 204 of
+    # 256x256 (1 round, 1.6)
+    assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_realign<256,256,32>"
+    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 6.4
+    odd = {(4095, 4095, 4095): 15, (5000, 5000, 999): 15, (2049, 4095, 511): 15,
+           (4607, 4607, 999): 2}                       # 1296 tiles: 3 rounds against 324: 3.2
+    for (M, N, K), want in odd.items():
+        assert plan(M, N, K)["variant"] == want, (M, N, K)
     # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU
     p = plan(2047, 2047, 2047)
     assert p["name"] == "mmrelu_bf16_any<128,128,32>" and p["grid"] == 16 * 16
@@ -473,3 +480,4 @@ def test_planner_cost_model_uses_skinny_tiles_where_large_tiles_idle_cus():
     # unaligned layouts keep the tile kernels (the skinny ones need 16-byte rows)
     p = mm.mmrelu_plan(F, 512, 511, 8192, 8192, 511, 511, cus=256)
     assert "unaligned" in p["name"]
+

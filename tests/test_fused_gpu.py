@@ -89,7 +89,7 @@ def variants(dtype):
 def accepts(dtype, v, N, K, lda, ldb, ldc, M=1):
     plan = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)
     name = plan["name"]
-    if "simple" in name or "unaligned" in name or "gemv" in name or "_any<" in name:
+    if "simple" in name or "unaligned" in name or "gemv" in name or "_any<" in name or "_realign<" in name:
         return True
     q = 4 if dtype == mm.DTYPE_F32 else 8
     return all(x % q == 0 for x in (N, K, lda, ldb, ldc))

@@ -81,7 +81,7 @@ def launch(dtype, variant, da, db, c_ptr, M, N, K, lda, ldb, ldc):
 # (dtype, M, N, K, ld, variants): None is the planner's choice. fp32: 1, 3
 # the aligned 128/64 tiles, 2 the unaligned 128 tile, 12 the 64x64 skinny
 # tile; bf16: 1 and 3 the ping-pong tiles (256 and 128 rows), 4 the 128
-# tile, 12 the 64x64 skinny tile, 2/13 the any-layout tiles (128, 64);
+# tile, 12 the 64x64 skinny tile, 2/13/15 the any-layout tiles (128, 64, 256);
 # N = 1 the matrix-vector kernel; M = 40 the few-rows skinny rule.
 CASES = [
     ("f32", 300, 264, 136, LD, [None, 1, 2, 3, 12]),
@@ -90,7 +90,7 @@ CASES = [
     ("bf16", 300, 264, 136, LD, [None, 1, 3, 4, 12]),
     ("bf16", 40, 264, 136, LD, [None]),
     ("bf16", 300, 1, 136, LD, [None]),
-    ("bf16", 300, 264, 136, LD - 1, [None, 2, 13]),
+    ("bf16", 300, 264, 136, LD - 1, [None, 2, 13, 15]),
 ]
 
 

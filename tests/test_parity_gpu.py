@@ -97,7 +97,7 @@ def variants(dtype):
 def accepts(dtype, v, N, K, lda, ldb, ldc, M=1):
     plan = mm.mmrelu_plan_variant(dtype, v, 8, 8, 8, 8, 8, 8)
     name = plan["name"]
-    if "simple" in name or "unaligned" in name or "gemv" in name or "_any<" in name:
+    if "simple" in name or "unaligned" in name or "gemv" in name or "_any<" in name or "_realign<" in name:
         return True
     q = 4 if dtype == mm.DTYPE_F32 else 8
     return all(x % q == 0 for x in (N, K, lda, ldb, ldc))
@@ -209,10 +209,10 @@ def placed(x: np.ndarray, off: int, ld: int):
 # (dtype, element offsets of A, B, C, variants). Only element alignment is
 # required of pointers; these start A, B and C 1..7 elements past a 16-byte
 # boundary, through the planner (None) and the kernels that accept such
-# layouts: bf16 2/13 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
+# layouts: bf16 2/13/15 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
 # 11 (matrix-vector) and 0.
-MISALIGNED = [("bf16", (1, 3, 5), [None, 2, 13, 0]), ("bf16", (7, 2, 0), [None, 2, 13]),
-              ("bf16", (0, 0, 3), [None, 13]), ("f32", (1, 2, 3), [None, 2, 4, 0]), ("f32", (3, 0, 1), [None, 2, 4])]
+MISALIGNED = [("bf16", (1, 3, 5), [None, 2, 13, 15, 0]), ("bf16", (7, 2, 0), [None, 2, 13, 15]),
+              ("bf16", (0, 0, 3), [None, 13, 15]), ("f32", (1, 2, 3), [None, 2, 4, 0]), ("f32", (3, 0, 1), [None, 2, 4])]
 
 
 @pytest.mark.parametrize("dtype,offs,vs", MISALIGNED, ids=[f"{m[0]}-{m[1]}" for m in MISALIGNED])
@@ -322,9 +322,11 @@ def test_deterministic_repeats(dtype):
 
 # (dtype, variant, shape): the tile kernels on grids of several waves. bf16 1
 # and 3 are the ping-pong tiles (an LDS ring per operand, the two wave
-# groups swapping roles at every barrier), 4 the 128 x 128 tile; fp32 1 the
-# aligned 128 x 128 tile, 4 the unaligned 64 x 64 tile.
+# groups swapping roles at every barrier), 4 the 128 x 128 tile, 15 the
+# any-layout 256 x 256 tile; fp32 1 the aligned 128 x 128 tile, 4 the
+# unaligned 64 x 64 tile.
 DETERMINISM = [("bf16", 1, (4352, 4352, 520)), ("bf16", 3, (4352, 4352, 520)), ("bf16", 4, (4352, 4352, 520)),
+               ("bf16", 15, (4352, 4352, 520)),
                ("f32", 1, (4352, 4352, 264)), ("f32", 4, (4352, 4352, 264))]
 
 
@@ -433,10 +435,11 @@ def small_int_inputs(cfg, seed):
 # (config, dtype, variant): the workloads' shapes and leading dimensions on
 # small-integer inputs, through the planner (None) and, for the ragged shape
 # with odd leading dimensions, every kernel that accepts that layout: fp32 2
-# and 4 (unaligned 128 and 64 tiles), bf16 2 and 13 (any-layout 128 and 64
-# tiles), and the plain kernel 0.
+# and 4 (unaligned 128 and 64 tiles), bf16 2, 13 and 15 (any-layout 128, 64
+# and 256 tiles), and the plain kernel 0.
 EXACT = [(1, "f32", None), (2, "f32", None), (3, "f32", None), (4, "f32", None), (4, "f32", 2), (4, "f32", 4),
-         (4, "f32", 0), (4, "bf16", None), (4, "bf16", 13), (4, "bf16", 0), (5, "bf16", None)]
+         (4, "f32", 0), (4, "bf16", None), (4, "bf16", 2), (4, "bf16", 13), (4, "bf16", 15), (4, "bf16", 0),
+         (5, "bf16", None)]
 
 
 @pytest.mark.parametrize("ident,dtype,variant", EXACT, ids=[f"C{i}-{d}-v{v}" for i, d, v in EXACT])
@@ -487,9 +490,11 @@ def run_fused(act, a, b, bias, M, N, K, variant):
 # and a grid of several bands of tile rows, with more tiles than XCDs and a
 # tile count that is not a multiple of eight (so both the regrouped ids and
 # the tail walk their bands). bf16: 1, 3 ping-pong tiles, 4 the 128 x 128
-# tile; fp32: 1, 2 the 128 x 128 tiles, 3, 4 the 64 x 64 tiles.
+# tile, 15 the any-layout 256 x 256 tile; fp32: 1, 2 the 128 x 128 tiles, 3,
+# 4 the 64 x 64 tiles.
 MULTIBAND = (2312, 2320, 200)
-TILE_KERNELS = [("bf16", 1), ("bf16", 3), ("bf16", 4), ("f32", 1), ("f32", 2), ("f32", 3), ("f32", 4)]
+TILE_KERNELS = [("bf16", 1), ("bf16", 3), ("bf16", 4), ("bf16", 15), ("f32", 1), ("f32", 2), ("f32", 3),
+                ("f32", 4)]
 EPILOGUES = [("relu", False), ("gelu_tanh", True), ("none", True)]
 
 
@@ -542,3 +547,62 @@ def test_tile_kernels_multiband_exact_integers(dtype, variant):
         np.testing.assert_array_equal(c.astype(np.float64), r)
     else:
         np.testing.assert_array_equal(c, bf16_round_ref(r))
+
+
+# --- the any-layout bf16 kernels on odd layouts over several bands ------------
+
+# 2313 x 2317 x 233 with lda = 235, ldb = 2319, ldc = 2321 (all odd) and A, B,
+# C starting 1, 2, 3 elements past a 16-byte boundary: rows of A and B start
+# on alternate halves of 4-byte words, the last slab holds 9 k, and the grid
+# has several bands of tiles. bf16 15 copies 4-byte words and realigns the
+# late rows in LDS; 2 and 13 realign in registers.
+ODD_SHAPE, ODD_LD, ODD_OFFS = (2313, 2317, 233), (235, 2319, 2321), (1, 2, 3)
+
+
+def run_odd_layout(act, a, b, bias, variant):
+    M, N, K = ODD_SHAPE
+    lda, ldb, ldc = ODD_LD
+    fa, pa = placed(a, ODD_OFFS[0], lda)
+    fb, pb = placed(b, ODD_OFFS[1], ldb)
+    fc, pc = placed(np.zeros((M, 0), np.uint16), ODD_OFFS[2], ldc)       # all NaN
+    dbias = to_dev(bias) if bias is not None else None
+    code = {"relu": mm.ACT_RELU, "gelu_tanh": mm.ACT_GELU_TANH, "none": mm.ACT_NONE}[act]
+    rc = mm.mmrelu_fused_bf16_variant(variant, code, pa, pb, dbias.data_ptr() if dbias is not None else 0, pc,
+                                      M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+    assert rc == mm.MMRELU_OK, mm.status_string(rc)
+    torch.cuda.synchronize()
+    whole = to_host(fc)
+    c = whole[ODD_OFFS[2]:ODD_OFFS[2] + M * ldc].reshape(M, ldc)
+    pad = np.concatenate([c[:, N:].ravel(), whole[:ODD_OFFS[2]], whole[ODD_OFFS[2] + M * ldc:]])
+    assert np.all(np.isnan(datagen.bf16_bits_to_f32(pad))), "wrote outside C"
+    return c[:, :N]
+
+
+@pytest.mark.parametrize("variant", [15, 2, 13])
+def test_any_layout_odd_multiband_exact_integers(variant):
+    """Small integers and an integer bias on the odd layout: bit-exact against
+    the oracle rounded to nearest-even."""
+    M, N, K = ODD_SHAPE
+    a = datagen.f32_to_bf16_bits(datagen.small_int_f32(3600 + variant, M, K))
+    b = datagen.f32_to_bf16_bits(datagen.small_int_f32(3700 + variant, K, N))
+    bias = datagen.f32_to_bf16_bits(datagen.small_int_f32(3800 + variant, 1, N).ravel())
+    print(f"odd layout exact variant={variant}", flush=True)
+    c = run_odd_layout("none", a, b, bias, variant)
+    np.testing.assert_array_equal(c, bf16_round_ref(oracle.fused("none", a, b, bias)))
+
+
+@pytest.mark.parametrize("variant", [15, 2])
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
+def test_any_layout_odd_multiband_normal(variant, act):
+    """Normal inputs with a bias on the odd layout, every element against the
+    oracle's fused form (bf16 tolerances of the fused tests)."""
+    M, N, K = ODD_SHAPE
+    a = datagen.f32_to_bf16_bits(datagen.normal_f32(3900 + variant, M, K, 1 / math.sqrt(K)))
+    b = datagen.f32_to_bf16_bits(datagen.normal_f32(4000 + variant, K, N, 1 / math.sqrt(K)))
+    bias = datagen.f32_to_bf16_bits(datagen.normal_f32(4100 + variant, 1, N, 0.5).ravel())
+    print(f"odd layout normal variant={variant} act={act}", flush=True)
+    c = datagen.bf16_bits_to_f32(run_odd_layout(act, a, b, bias, variant)).astype(np.float64)
+    r = oracle.fused(act, a, b, bias)
+    assert np.all(np.isfinite(c))
+    assert np.linalg.norm(c - r) / np.linalg.norm(r) <= 1e-2
+    assert np.all(np.abs(c - r) <= 2.0 ** -8 * np.abs(r) + 4e-6), np.abs(c - r).max()

@@ -1,0 +1,458 @@
+// bf16 act(A·B + bias) on the gfx950 matrix cores for any layout, fed by the
+// buffer unit's direct global->LDS copies of 4-byte words.
+//
+// The lecture's tiled recipe ("Kernels, Triton, XLA", section "Reductions and
+// tiling"): one workgroup per output tile, K swept in slabs staged in LDS,
+// masked loads that read zeros past the edges, fp32 accumulation, the
+// activation on the accumulator, one masked store.
+//
+// Layouts the 16-byte kernels do not take (odd leading dimensions, N or K not
+// multiples of 8, rows that start anywhere on a 2-byte boundary) are staged
+// in two steps:
+//  * Copy: each operand row's window of the slab is copied as 4-byte words,
+//    from the word boundary at or below the row's first element, straight
+//    into LDS (buffer_load_dword ... lds). A row whose first element is the
+//    upper half of a word lands one element late: its window holds one
+//    element before the slab and lacks the slab's last one, which one more
+//    word per such row (its side word) brings in.
+//  * Realign: once a slab has landed, the lanes rewrite the late rows in
+//    place, each 16-byte chunk joined with the first word of the next chunk
+//    (or the side word) and shifted down by one element (v_alignbyte). Rows
+//    then sit exactly where the 16-byte kernels put theirs, and the
+//    fragment reads are theirs: one ds_read_b128 per A fragment, two
+//    ds_read_b64_tr_b16 per B fragment.
+// Whether a row is late depends on the row only (slabs start at multiples of
+// 32 elements, so k0 * ld is even): the plan is made once per tile.
+//
+// Tile 256 x 256 per workgroup of eight waves (2 x 4), each a 128 x 64
+// sub-tile of 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128 fp32
+// accumulators per lane); K in slabs of 32 in a ring of four LDS stages. In
+// step kt every wave multiplies slab kt (fragments in registers), reads slab
+// kt+1's fragments, realigns slab kt+2 and issues the copies of slab kt+4
+// into the stage slab kt left; one barrier per step.
+//
+// LDS stage (34 KB): A, 256 rows x 64 bytes, chunk c of row r at r*64 +
+// 16 (c ^ (r/4 % 4)); B, 32 rows x 512 bytes, chunk c of row k at k*512 +
+// 16 (c ^ swz_b(k)); then the side words, A's (one per row) and B's (one per
+// slab row). Each copy instruction fills 256 contiguous bytes: four A rows,
+// half a B row, or a block of side words.
+//
+// Edges: rows past M and B rows past K get out-of-range offsets (the copy
+// writes zeros); A elements past K in the last slab are zeroed while
+// realigning (the words there hold the next row's elements); B columns past N
+// hold whatever follows in memory and only reach outputs past N, which are
+// never stored. Each resource ends at the word that holds the operand's last
+// element, and a 4-byte word never crosses a page, so the bytes read around
+// an operand are always mapped. Outputs are stored one element at a time, so
+// any ldc works.
+#include <type_traits>
+
+#include "kernels.hpp"
+#include "device_common.hpp"
+#include "../../include/mmrelu.h"
+
+namespace mmrelu {
+namespace {
+
+constexpr int kTile = 256, kSlab = 32, kThreads = 512, kStages = 4;
+constexpr int kMB = 8, kNB = 4;                          // MFMA blocks per wave: 128 rows x 64 columns
+constexpr int kABytes = kTile * kSlab * 2;               // A part of a stage
+constexpr int kBBytes = kSlab * kTile * 2;               // B part
+constexpr int kSideA = kABytes + kBBytes;                // A's side words, one per tile row
+constexpr int kSideB = kSideA + kTile * 4;               // B's side words, one per slab row
+constexpr int kStageBytes = kSideA + 8 * 256;            // side block: one 256-byte copy per wave
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+
+__device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+__device__ inline uint32_t a_byte(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+__device__ inline uint32_t b_byte(int k, int c) { return kABytes + k * 512 + 16 * (c ^ swz_b(k)); }
+
+// The 8 elements that start one element into the 18 bytes lo:next (element
+// j of the result is element j+1 of the pair).
+__device__ inline u32x4 shift_down(const u32x4 &lo, uint32_t next)
+{
+    u32x4 out;
+    out[0] = __builtin_amdgcn_alignbyte(lo[1], lo[0], 2);
+    out[1] = __builtin_amdgcn_alignbyte(lo[2], lo[1], 2);
+    out[2] = __builtin_amdgcn_alignbyte(lo[3], lo[2], 2);
+    out[3] = __builtin_amdgcn_alignbyte(next, lo[3], 2);
+    return out;
+}
+
+// Keep the first v of the 8 elements in x (v <= 0: none), zero the rest.
+__device__ inline u32x4 keep_first(u32x4 x, int v)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (0u - static_cast<uint32_t>(2 * j < v)) & 0x0000FFFFu;
+        const uint32_t hi = (0u - static_cast<uint32_t>(2 * j + 1 < v)) & 0xFFFF0000u;
+        x[j] &= lo | hi;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N, int K,
+    int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m, const uint16_t *__restrict__ bias,
+    int act)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int g = lane >> 4, t = lane & 15;
+
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * kTile, n0 = tn * kTile;
+    const int rows = M - m0;                              // valid tile rows (may exceed 256)
+    const uint32_t lds0 = lds_address(lds);
+
+    // Word bases. Row r of the tile starts a_mis + r lda elements past A's
+    // word base; row k of slab k0, b_mis + k ldb past the word base of B's
+    // slab (k0 ldb is even, so b_mis is the same for every slab).
+    const uintptr_t a_addr = reinterpret_cast<uintptr_t>(A + static_cast<int64_t>(m0) * lda);
+    const uintptr_t b_addr = reinterpret_cast<uintptr_t>(B + n0);
+    const int a_mis = static_cast<int>((a_addr >> 1) & 1), b_mis = static_cast<int>((b_addr >> 1) & 1);
+    const rsrc_t ra = make_rsrc(reinterpret_cast<const void *>(a_addr & ~uintptr_t{3}),
+                                ((a_mis + static_cast<int64_t>(rows - 1) * lda + K) * 2 + 3) & ~int64_t{3});
+    auto b_rsrc = [&](int k0) __attribute__((always_inline)) {
+        const uintptr_t base = (b_addr + static_cast<uintptr_t>(static_cast<int64_t>(k0) * ldb * 2)) & ~uintptr_t{3};
+        return make_rsrc(reinterpret_cast<const void *>(base),
+                         ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3});
+    };
+    // First word of row r's window (byte offset from the word base, k0 = 0),
+    // and whether the row is late.
+    auto a_word0 = [&](int r) { return static_cast<uint32_t>(((a_mis + static_cast<int64_t>(r) * lda) >> 1) * 4); };
+    auto a_late = [&](int r) { return ((a_mis + static_cast<int64_t>(r) * lda) & 1) != 0; };
+    auto b_word0 = [&](int k) { return static_cast<uint32_t>(((b_mis + static_cast<int64_t>(k) * ldb) >> 1) * 4); };
+    auto b_late = [&](int k) { return ((b_mis + static_cast<int64_t>(k) * ldb) & 1) != 0; };
+
+    // Copy plans. A copy moves 16 bytes a lane (1 KB an instruction) from
+    // any 4-byte boundary (buffer loads of a dword or more need only 4-byte
+    // alignment), or, near the end of an operand, 4 bytes a lane: a 16-byte
+    // copy that would straddle the end of its resource's range is never
+    // issued (see `risky`). Either way wave w fills the same LDS bytes.
+    //  A copy q (0, 1) of wave w fills rows 128q + 16w + l/4, stored chunk
+    //  l%4 = the row's chunk l%4 ^ (l/16 % 4); row 128q + r's window starts
+    //  256 q lda bytes after row r's. As four 4-byte copies d = 0..3, copy d
+    //  fills rows 128q + 16w + 4d + l/16, stored chunk (l/4)%4, the row's
+    //  chunk (l/4)%4 ^ d, word l%4.
+    //  B copy q fills slab rows 16q + 2w + l/32, stored chunk l%32 = the
+    //  row's chunk l%32 ^ swz_b(row), where swz_b(16q + r) = swz_b(r); row
+    //  16q + r's window starts 32 q ldb bytes after row r's. As four 4-byte
+    //  copies, copy d fills half d%2 of row 16q + 2w + d/2: stored chunk
+    //  16 (d%2) + l/4, word l%4.
+    const int ax_row0 = 16 * wave + (lane >> 2);
+    const uint32_t ax_v0 = a_word0(ax_row0) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    const int bx_row0 = 2 * wave + (lane >> 5);
+    const uint32_t bx_v0 = b_word0(bx_row0) + 16 * ((lane & 31) ^ swz_b(bx_row0));
+    const int an_row0 = 16 * wave + (lane >> 4);
+    const uint32_t an_v0 = a_word0(an_row0) + 4 * (lane & 3);
+    // Side words: wave w's block holds words 64w .. 64w+63; words 0-255 are A
+    // rows' (word 16 of the window), 256-287 B slab rows' (word 128).
+    const int sd = 64 * wave + lane;
+    uint32_t side_v = kOutOfRange;
+    if (sd < kTile) {
+        if (sd < rows && a_late(sd)) side_v = a_word0(sd) + 64;
+    } else if (sd < kTile + kSlab) {
+        if (b_late(sd - kTile)) side_v = b_word0(sd - kTile) + 512;
+    }
+    const bool side_b = wave == 4;
+    // Byte ranges of the A resource and of the B resource of slab k0.
+    const int64_t a_range = ((a_mis + static_cast<int64_t>(rows - 1) * lda + K) * 2 + 3) & ~int64_t{3};
+    auto b_range = [&](int k0) {
+        return ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3};
+    };
+
+    const int nk = (K + kSlab - 1) / kSlab;
+    // The per-lane copy offsets pass through an empty asm once per slab, so
+    // the compiler derives the offsets (and the edge tests) anew for each
+    // slab instead of keeping them all live across the K loop.
+    struct CopyPlan {
+        uint32_t ax, bx, an, side;
+        int ax_row, an_row;
+    };
+    auto copy_plan = [&]() __attribute__((always_inline)) {
+        CopyPlan c{ax_v0, bx_v0, an_v0, side_v, ax_row0, an_row0};
+        asm volatile("" : "+v"(c.ax), "+v"(c.bx), "+v"(c.an), "+v"(c.side), "+v"(c.ax_row), "+v"(c.an_row));
+        return c;
+    };
+    // Whether some 16-byte copy of this wave for slab s would straddle the
+    // end of its resource's range (the same for the whole wave). Such a slab
+    // is copied 4 bytes a lane: every 4-byte word is then wholly in range or
+    // wholly out, and no byte past an operand's last word is read.
+    auto risky = [&](int s, const CopyPlan &cp) __attribute__((always_inline)) {
+        const int k0 = s * kSlab;
+        const int64_t rb_end = b_range(k0);
+        bool r = false;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int64_t oa = static_cast<int64_t>(cp.ax) + 256 * q * lda + 2 * k0;
+            r |= cp.ax_row + 128 * q < rows && oa < a_range && oa + 16 > a_range;
+            const int64_t ob = static_cast<int64_t>(cp.bx) + 32 * q * ldb;
+            r |= k0 + bx_row0 + 16 * q < K && ob < rb_end && ob + 16 > rb_end;
+        }
+        return s < nk && __builtin_amdgcn_ballot_w64(r) != 0;
+    };
+    // Copy q of slab s (zero fills for slabs past K) into stage s % 4; 16-byte
+    // copies q = 0, 1 (A), 2, 3 (B), 4 (side words); 4-byte copies q = 4c + d
+    // for the 16-byte copy c < 4, and 16 (side words). (Selects, not
+    // branches.)
+    constexpr int kCopiesWide = 5, kCopiesNarrow = 17;
+    auto issue_copy = [&](auto wide_c, int q, int s, const rsrc_t &rb, const CopyPlan &cp)
+                          __attribute__((always_inline)) {
+        constexpr bool kWide = decltype(wide_c)::value;
+        constexpr int kSide = kWide ? kCopiesWide - 1 : kCopiesNarrow - 1;
+        const bool live = s < nk;
+        const int k0 = s * kSlab;
+        const uint32_t st = lds0 + (s & (kStages - 1)) * kStageBytes;
+        if (q == kSide) {
+            const bool ok = live && cp.side != kOutOfRange && (!side_b || k0 + lane < K);
+            const uint32_t off = side_b ? cp.side : cp.side + static_cast<uint32_t>(2 * k0);
+            load_to_lds<4>(side_b ? rb : ra, st + kSideA + wave * 256, ok ? off : kOutOfRange);
+        } else if (kWide && q < 2) {
+            const bool ok = live && cp.ax_row + 128 * q < rows;
+            const uint32_t off = cp.ax + static_cast<uint32_t>(256 * q * lda + 2 * k0);
+            load_to_lds<16>(ra, st + (8 * q + wave) * 1024, ok ? off : kOutOfRange);
+        } else if (kWide) {
+            const int qq = q - 2;
+            const bool ok = live && k0 + bx_row0 + 16 * qq < K;
+            const uint32_t off = cp.bx + static_cast<uint32_t>(32 * qq * ldb);
+            load_to_lds<16>(rb, st + kABytes + (8 * qq + wave) * 1024, ok ? off : kOutOfRange);
+        } else if (q < 8) {
+            const int c = q >> 2, d = q & 3;
+            const bool ok = live && cp.an_row + 128 * c + 4 * d < rows;
+            const uint32_t off = cp.an + static_cast<uint32_t>((256 * c + 8 * d) * lda + 2 * k0) +
+                                 16 * (((lane >> 2) & 3) ^ d);
+            load_to_lds<4>(ra, st + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+        } else {
+            const int c = (q >> 2) - 2, d = q & 3;
+            const int row = 2 * wave + (d >> 1);                 // of the slab, less 16 c
+            const bool ok = live && k0 + row + 16 * c < K;
+            const uint32_t off = b_word0(row) + static_cast<uint32_t>(32 * c * ldb) +
+                                 16 * ((16 * (d & 1) + (lane >> 2)) ^ swz_b(row)) + 4 * (lane & 3);
+            load_to_lds<4>(rb, st + kABytes + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+        }
+    };
+    using Wide = std::integral_constant<bool, true>;
+    using Narrow = std::integral_constant<bool, false>;
+    auto issue_slab = [&](int s) __attribute__((always_inline)) {
+        const rsrc_t rb = b_rsrc(s * kSlab);
+        const CopyPlan cp = copy_plan();
+        if (!risky(s, cp)) {
+#pragma unroll
+            for (int q = 0; q < kCopiesWide; ++q) issue_copy(Wide{}, q, s, rb, cp);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kCopiesNarrow; ++q) issue_copy(Narrow{}, q, s, rb, cp);
+        }
+    };
+
+    // Realign plan. A: wave w rewrites rows 32w + 16j + l/4 (j = 0, 1),
+    // chunk l%4; the next chunk's first word, or the side word for the last
+    // chunk. B: rows 4w + 2j + l/32, chunk l%32. Row + 16 (A) and row + 2
+    // (B) have the same lateness (16 lda and 2 ldb are even).
+    const int ra_row = 32 * wave + (lane >> 2), ra_c = lane & 3;
+    const bool ra_late = a_late(ra_row);
+    const uint32_t ra_main = a_byte(ra_row, ra_c);                                 // + 1024 j
+    const uint32_t ra_next = ra_c < 3 ? a_byte(ra_row, ra_c + 1) : kSideA + 4 * ra_row;
+    const uint32_t ra_step = ra_c < 3 ? 1024u : 64u;
+    const int rb_row = 4 * wave + (lane >> 5), rb_c = lane & 31;
+    const bool rb_late = b_late(rb_row);
+    uint32_t rb_main[2], rb_next[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        rb_main[j] = b_byte(rb_row + 2 * j, rb_c);
+        rb_next[j] = rb_c < 31 ? b_byte(rb_row + 2 * j, rb_c + 1) : kSideB + 4 * (rb_row + 2 * j);
+    }
+    // All reads of a wave's units come before its writes: a unit's next
+    // word belongs to a unit of the same wave, which is rewritten after.
+    auto realign = [&](int s) __attribute__((always_inline)) {
+        uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
+        const int k0 = s * kSlab;
+        const bool tail = K - k0 < kSlab;
+        if (ra_late || tail) {
+            u32x4 v[2];
+            uint32_t x[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v[j] = *reinterpret_cast<const u32x4 *>(st + ra_main + 1024 * j);
+                x[j] = *reinterpret_cast<const uint32_t *>(st + ra_next + ra_step * j);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (ra_late) v[j] = shift_down(v[j], x[j]);
+                if (tail) v[j] = keep_first(v[j], K - k0 - 8 * ra_c);
+                *reinterpret_cast<u32x4 *>(st + ra_main + 1024 * j) = v[j];
+            }
+        }
+        if (rb_late) {
+            u32x4 v[2];
+            uint32_t x[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v[j] = *reinterpret_cast<const u32x4 *>(st + rb_main[j]);
+                x[j] = *reinterpret_cast<const uint32_t *>(st + rb_next[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4 *>(st + rb_main[j]) = shift_down(v[j], x[j]);
+        }
+    };
+
+    // Fragment reads. A block i: rows wm*128 + 16i + t, chunk g; B block j:
+    // lane t of group g addresses slab row 8g + t/4 (+4 for the second
+    // half) at columns wn*64 + 16j + 4(t%4) .. +3.
+    const uint32_t a_frag = a_byte(wm * 128 + t, g);                              // + 1024 i
+    uint32_t b_frag[kNB];
+    {
+        const int k_lane = 8 * g + (t >> 2);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+            const int n = wn * 64 + j * 16 + 4 * (t & 3);
+            b_frag[j] = b_byte(k_lane, n >> 3) + 2 * (n & 7);
+        }
+    }
+    // A fragments are held once: block i of slab kt+1 is read right after
+    // the four MFMAs of slab kt that use block i. B fragments are held twice
+    // (slab kt's are used by every A block): fb, and fb_next for slab kt+1.
+    bf16x8 fa[kMB], fb[kNB], fb_next[kNB];
+    auto load_frag_a = [&](int s, int i) __attribute__((always_inline)) {
+        const uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
+        fa[i] = *reinterpret_cast<const bf16x8 *>(st + a_frag + 1024 * i);
+    };
+    auto load_frag_b = [&](bf16x8 &dst, int s, int j) __attribute__((always_inline)) {
+        const uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
+        i16x4 half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMRELU_LDS i16x4 *)(st + b_frag[j] + 4 * 512 * h));
+        dst = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x4 acc[kMB][kNB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mfma_row = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    };
+
+    // Step kt (slab kt+1 exists): wait for slab kt+2 (slab kt+3 may stay in
+    // flight; waiting for all but the 16-byte count of one slab over-waits
+    // after a slab of 4-byte copies, which is harmless), barrier; then eight
+    // parts, one per A block i: the four MFMAs of block i of slab kt, the
+    // read of block i of slab kt+1 and, in every other part, one B fragment
+    // of slab kt+1. After part 0 the copies of slab kt+4 (into slab kt's
+    // stage) are issued, after part 1 slab kt+2 is realigned, while the
+    // matrix cores work through the MFMAs issued so far. The fences keep each
+    // part's MFMAs inside the part, ahead of the read that overwrites their
+    // operand.
+    auto step = [&](int kt) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kCopiesWide>();
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            mfma_row(i);
+            load_frag_a(kt + 1, i);
+            if ((i & 1) == 0) load_frag_b(fb_next[i >> 1], kt + 1, i >> 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the LDS reads
+            __builtin_amdgcn_sched_barrier(0);
+            if (i == 0) issue_slab(kt + 4);
+            if (i == 1 && kt + 2 < nk) realign(kt + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) fb[j] = fb_next[j];
+    };
+    if (nk > 0) {
+        issue_slab(0);
+        issue_slab(1);
+        issue_slab(2);
+        wait_vmcnt<kCopiesWide>();                        // slabs 0 and 1 have landed
+        __syncthreads();
+        realign(0);
+        if (nk > 1) realign(1);
+        issue_slab(3);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) load_frag_b(fb[j], 0, j);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) load_frag_a(0, i);
+        for (int kt = 0; kt + 1 < nk; ++kt) step(kt);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) mfma_row(i);
+        wait_vmcnt<0>();                                  // the zero fills past K
+    }
+
+    // Epilogue: lane (g, t) of block (i, j) holds C[row][col .. col+3]; bias
+    // and activation on fp32, one rounding to bf16, one 2-byte masked store
+    // per element.
+    const __amdgpu_buffer_rsrc_t rc =
+        make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0, (static_cast<int64_t>(rows - 1) * ldc + N - n0) * 2);
+    float bj[kNB][4];
+    if (bias != nullptr) {
+        const __amdgpu_buffer_rsrc_t rbias = make_bias_rsrc(bias, n0, N, 2);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rbias, wn * 64 + j * 16 + 4 * g + r);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
+    }
+    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            const int row = wm * 128 + i * 16 + t;
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) {
+                const int col = wn * 64 + j * 16 + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const __bf16 o = static_cast<__bf16>(activate<ACT>(acc[i][j][r] + bj[j][r]));
+                    const uint32_t off = (row < rows && n0 + col + r < N)
+                                             ? static_cast<uint32_t>((row * ldc + col + r) * 2)
+                                             : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, o), rc, off, 0, 0);
+                }
+            }
+        }
+    });
+}
+
+// Tile-row bands of this height are walked column by column inside each
+// XCD's range of tiles (tile_of).
+constexpr int kGroupM = 8;
+
+hipError_t launch_realign(const Problem &p, int64_t grid, hipStream_t stream)
+{
+    const int tiles_m = (p.M + kTile - 1) / kTile, tiles_n = (p.N + kTile - 1) / kTile;
+    hipLaunchKernelGGL(mmrelu_bf16_realign, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
+                       static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, kGroupM,
+                       static_cast<const uint16_t *>(p.bias), p.act);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// 256 x 256 tiles, any layout.
+const Variant *variant_bf16_realign()
+{
+    static const Variant v = {"mmrelu_bf16_realign<256,256,32>", MMRELU_DTYPE_BF16, kTile, kTile, kSlab, kThreads,
+                              1, 0, launch_realign, 1.0f};
+    return &v;
+}
+
+}  // namespace mmrelu

@@ -57,6 +57,9 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks);
 const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 // bf16 matrix-core kernel for any layout (k_bf16_any.hip).
 const Variant *variant_bf16_any(int bt);   // bt = 64 or 128
+// bf16 matrix-core kernel for any layout fed by 4-byte copies to LDS
+// (k_bf16_realign.hip): 256 x 256 tiles.
+const Variant *variant_bf16_realign();
 // One wave per output (k_gemv.hip): matrix-vector products (N = 1), any layout.
 const Variant *variant_f32_gemv();
 const Variant *variant_bf16_gemv();

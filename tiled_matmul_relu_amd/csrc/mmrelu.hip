@@ -17,10 +17,11 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 15;
-constexpr int kNumBf16 = 15;
+constexpr int kNumBf16 = 16;
 // Both tables: 0 the plain kernel; 1 the large aligned tile and 2 the large
 // tile for any layout; 3 and 4 smaller tiles; 5 - 10 and 12 the skinny
-// tiles; 11 the matrix-vector kernel; 13 and 14 the rest.
+// tiles; 11 the matrix-vector kernel; 13 and 14 the rest; bf16 15 the
+// 256 x 256 tile for any layout.
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
@@ -42,7 +43,7 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
-                                               variant_bf16_skinny(1, 4, 1)};
+                                               variant_bf16_skinny(1, 4, 1), variant_bf16_realign()};
     return t;
 }
 
@@ -115,7 +116,7 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
 // full tiles of block_m x block_n outputs at the variant's measured relative
 // cost per output (wave quantisation of the grid over the CUs). bf16
 // layouts the 16-byte-vector kernels do not accept go to the any-layout
-// matrix-core kernel (variants 2 and 13); the plain tiled kernel (variant 0) is
+// matrix-core kernels (variants 2, 13 and 15); the plain tiled kernel (variant 0) is
 // only reached through the _variant entry points.
 // Pointers are taken as 16-byte aligned when null (planning without buffers).
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -150,12 +151,21 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     if (dtype == MMRELU_DTYPE_F32) cand = fits ? f32_aligned : f32_any;
     else if (fits) cand = bf16_aligned;
     else {
-        // bf16, any layout, on the matrix cores: 128 x 128 tiles (variant 2)
-        // once their grid gives every CU one or more, else 64 x 64 tiles
-        // (variant 13), which keep more CUs busy (measured: 2047^3, 64.5
-        // against 76.7 us; 1001^3, 33.6 against 21.1 us).
+        // bf16, any layout, on the matrix cores: 64 x 64 tiles (variant 13)
+        // until the 128 x 128 grid gives every CU a tile, which keep more CUs
+        // busy (measured: 1001^3, 21.1 against 33.6 us for 128 x 128 tiles);
+        // then 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x
+        // 256 tiles (variant 15, one per CU), whichever has the shorter
+        // estimate: rounds of the grid over the CUs, a round of 256 x 256
+        // tiles taking 1.6 rounds of 128 x 128 (measured at K = 2049: 123
+        // and 77 us; 4097 x 3001 x 2049: 123 against 154 us, 8191^3: 1589
+        // against 1975 us, 2047^3: 112 against 62 us).
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        return tiles128 >= static_cast<int64_t>(cus) ? 2 : 13;
+        const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (tiles128 < static_cast<int64_t>(cus)) return 13;
+        const double t2 = static_cast<double>((tiles128 + 2 * cus - 1) / (2 * cus));
+        const double t15 = 1.6 * static_cast<double>((tiles256 + cus - 1) / cus);
+        return t15 < t2 ? 15 : 2;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
     // seven skinny tiles (variants 5 - 10 and 12), which split K over eight
