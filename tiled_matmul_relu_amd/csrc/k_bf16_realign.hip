@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     }
     // All reads of a wave's units come before its writes: a unit's next
     // word belongs to a unit of the same wave, which is rewritten after.
-    auto realign = [&](int s) __attribute__((always_inline)) {
+    auto realign_a = [&](int s) __attribute__((always_inline)) {
         uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
         const int k0 = s * kSlab;
         const bool tail = K - k0 < kSlab;
@@ -288,6 +288,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
                 *reinterpret_cast<u32x4 *>(st + ra_main + 1024 * j) = v[j];
             }
         }
+    };
+    auto realign_b = [&](int s) __attribute__((always_inline)) {
+        uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
         if (rb_late) {
             u32x4 v[2];
             uint32_t x[2];
@@ -299,6 +302,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
 #pragma unroll
             for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4 *>(st + rb_main[j]) = shift_down(v[j], x[j]);
         }
+    };
+    auto realign = [&](int s) __attribute__((always_inline)) {
+        realign_a(s);
+        realign_b(s);
     };
 
     // Fragment reads. A block i: rows wm*128 + 16i + t, chunk g; B block j:
@@ -365,8 +372,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the LDS reads
             __builtin_amdgcn_sched_barrier(0);
-            if (i == 0) issue_slab(kt + 4);
-            if (i == 1 && kt + 2 < nk) realign(kt + 2);
+            if (i == 0 && kt + 2 < nk) realign(kt + 2);
+            if (i == 1) issue_slab(kt + 4);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll

@@ -157,14 +157,17 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
         // then 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x
         // 256 tiles (variant 15, one per CU), whichever has the shorter
         // estimate: rounds of the grid over the CUs, a round of 256 x 256
-        // tiles taking 1.6 rounds of 128 x 128 (measured at K = 2049: 123
-        // and 77 us; 4097 x 3001 x 2049: 123 against 154 us, 8191^3: 1589
-        // against 1975 us, 2047^3: 112 against 62 us).
+        // tiles counting 1.6 + 256 / K rounds of 128 x 128 (its start-up is a
+        // larger share at short K). Measured, variant 2 against 15:
+        // 4097 x 3001 x 2049 151 / 111 us, 3000^3 149 / 129, 5000^2 x 999
+        // 146 / 134, 4607^2 x 999 120 / 137, 2049 x 4095 x 511 43 / 46,
+        // 2047^3 61 / 103, 8191^3 1974 / 1459.
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
         if (tiles128 < static_cast<int64_t>(cus)) return 13;
         const double t2 = static_cast<double>((tiles128 + 2 * cus - 1) / (2 * cus));
-        const double t15 = 1.6 * static_cast<double>((tiles256 + cus - 1) / cus);
+        const double t15 = (1.6 + 256.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
+                           static_cast<double>((tiles256 + cus - 1) / cus);
         return t15 < t2 ? 15 : 2;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
