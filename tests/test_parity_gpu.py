@@ -606,3 +606,29 @@ def test_any_layout_odd_multiband_normal(variant, act):
     assert np.all(np.isfinite(c))
     assert np.linalg.norm(c - r) / np.linalg.norm(r) <= 1e-2
     assert np.all(np.abs(c - r) <= 2.0 ** -8 * np.abs(r) + 4e-6), np.abs(c - r).max()
+
+
+# Even leading dimensions with operands that start one element past a 4-byte
+# boundary: every row of A and B lands one element late in the 256 x 256
+# any-layout kernel's copies (variant 15), and none does with an even start;
+# through the planner, the register-shift kernel 2 and the plain kernel 0.
+@pytest.mark.parametrize("offs", [(1, 1, 1), (2, 2, 2), (3, 2, 1)], ids=["all-late", "none-late", "A-late"])
+@pytest.mark.parametrize("variant", [None, 15, 2, 0])
+def test_any_layout_even_leading_dims(offs, variant):
+    M, N, K = 520, 600, 166                              # K: the last slab holds 6 k
+    lda, ldb, ldc = K + 2, N + 2, N + 6                  # even, not multiples of 8
+    a = datagen.f32_to_bf16_bits(datagen.small_int_f32(4200, M, K))
+    b = datagen.f32_to_bf16_bits(datagen.small_int_f32(4201, K, N))
+    fa, pa = placed(a, offs[0], lda)
+    fb, pb = placed(b, offs[1], ldb)
+    fc, pc = placed(np.zeros((M, 0), np.uint16), offs[2], ldc)
+    print(f"even ld offs={offs} variant={variant}", flush=True)
+    args = (pa, pb, pc, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+    rc = mm.mmrelu_bf16(*args) if variant is None else mm.mmrelu_bf16_variant(variant, *args)
+    assert rc == mm.MMRELU_OK, mm.status_string(rc)
+    torch.cuda.synchronize()
+    whole = to_host(fc)
+    c = whole[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+    np.testing.assert_array_equal(c[:, :N], bf16_round_ref(oracle.mmrelu(a, b)))
+    pad = np.concatenate([c[:, N:].ravel(), whole[:offs[2]], whole[offs[2] + M * ldc:]])
+    assert np.all(np.isnan(datagen.bf16_bits_to_f32(pad))), "wrote outside C"
