@@ -14,10 +14,11 @@
 //    by every workgroup and stays in L2. A 64 x 64 tile (MB = NB = 4) serves
 //    small squares and long-K products with few output tiles, where it
 //    halves the operand bytes per output of the 32 x 64 tile.
-//  * Its eight waves split K into eight contiguous ranges of slabs and run
-//    independently, with no barrier inside the loop; the partial tiles are
-//    summed through LDS at the end (fixed order: deterministic results), one
-//    16 x 16 block per wave (two at 64 x 64).
+//  * Its eight waves (four for the 16 x 64 few-rows strips) split K into as
+//    many contiguous ranges of slabs and run independently, with no barrier
+//    inside the loop; the partial tiles are summed through LDS at the end
+//    (fixed order: deterministic results), one 16 x 16 block per wave (two
+//    at 64 x 64).
 //  * Both operands are issued kDepth slabs ahead of the slab being
 //    multiplied: A fragments straight into registers (each lane's 8 bf16 /
 //    4 fp32 of a row are contiguous), rotating through kDepth + 1 register
@@ -50,6 +51,8 @@
 namespace mmrelu {
 namespace {
 
+// Waves per workgroup: eight, or four for the 16 x 64 few-rows strips (see
+// their variants).
 constexpr int kWaves = 8, kThreads = kWaves * 64;
 
 template <typename T>
@@ -77,7 +80,7 @@ __device__ inline u32x4 load_b128_async(rsrc_t r, uint32_t voffset)
 
 // KS k blocks per slab (KS = 2: a row of A read in a step covers a whole
 // 128-byte line); kStages slabs in the ring, kStages - 1 of them in flight.
-template <typename T, int MB, int NB, int KS, int STAGES>
+template <typename T, int MB, int NB, int KS, int STAGES, int W>
 struct SkinnyShape {
     static constexpr int kBlkK = KBlock<T>::kK;
     static constexpr int kSlabK = KS * kBlkK;
@@ -86,22 +89,22 @@ struct SkinnyShape {
     static constexpr int kStageBytes = kSlabK * kRowBytes;         // KS * NB KB
     static constexpr int kStages = STAGES;
     static constexpr int kDepth = kStages - 1;                     // slabs in flight ahead
-    static constexpr int kRingBytes = kWaves * kStages * kStageBytes;
-    static constexpr int kRedBytes = kWaves * MB * NB * 64 * 16;   // partial tiles
+    static constexpr int kRingBytes = W * kStages * kStageBytes;
+    static constexpr int kRedBytes = W * MB * NB * 64 * 16;        // partial tiles
     static constexpr int kLdsBytes = kRingBytes > kRedBytes ? kRingBytes : kRedBytes;
     static_assert(kBlkK * kRowBytes == NB * 1024, "one 1 KB copy per 16 columns and k block");
     static_assert(kStages >= 2, "ring depth");
-    static_assert(MB * NB <= kWaves || (MB * NB) % kWaves == 0, "whole blocks per reducing wave");
+    static_assert(MB * NB <= W || (MB * NB) % W == 0, "whole blocks per reducing wave");
     static_assert(kDepth * KS * (NB + MB) <= 63, "vmcnt range");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int MB, int NB, int KS, int STAGES>
-__global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
+template <typename T, int MB, int NB, int KS, int STAGES, int W>
+__global__ __launch_bounds__(W * 64, 1) void mmrelu_skinny(
     const T *__restrict__ A, const T *__restrict__ B, T *__restrict__ C, int M, int N, int K,
     int64_t lda, int64_t ldb, int64_t ldc, const T *__restrict__ bias, int act)
 {
-    using S = SkinnyShape<T, MB, NB, KS, STAGES>;
+    using S = SkinnyShape<T, MB, NB, KS, STAGES, W>;
     constexpr int kSlabK = S::kSlabK, kBlkK = S::kBlkK, kEsize = S::kEsize, kRowBytes = S::kRowBytes;
     constexpr int kStageBytes = S::kStageBytes, kStages = S::kStages, kDepth = S::kDepth;
     constexpr int kSets = kDepth + 1;                  // A register sets = ring stages
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
 
     // This wave's slabs: a contiguous, balanced share of ceil(K / kSlabK).
     const int nk = (K + kSlabK - 1) / kSlabK;
-    const int s_begin = (nk * wave) / kWaves, s_end = (nk * (wave + 1)) / kWaves;
+    const int s_begin = (nk * wave) / W, s_end = (nk * (wave + 1)) / W;
     const int n_w = s_end - s_begin;
 
     // B copies: KS * NB 1 KB copies per slab; lane l of copy c fills LDS byte
@@ -276,10 +279,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     // tiles, two at 64 x 64).
     const __amdgpu_buffer_rsrc_t rc =
         make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0, ((static_cast<int64_t>(M) - 1 - m0) * ldc + N - n0) * kEsize);
-    for (int b = wave; b < kNBlk; b += kWaves) {
+    for (int b = wave; b < kNBlk; b += W) {
         f32x4 v = red[b * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += red[(w * kNBlk + b) * 64 + lane];
+        for (int w = 1; w < W; ++w) v += red[(w * kNBlk + b) * 64 + lane];
         const int i = b / NB, jb = b % NB;
         const int row = 16 * i + t;                    // within the tile
         const int col = 16 * jb + 4 * g;
@@ -315,10 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_skinny(
     }
 }
 
-template <typename T, int MB, int NB, int KS, int STAGES>
+template <typename T, int MB, int NB, int KS, int STAGES, int W = kWaves>
 hipError_t launch_skinny(const Problem &p, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mmrelu_skinny<T, MB, NB, KS, STAGES>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((mmrelu_skinny<T, MB, NB, KS, STAGES, W>), dim3(static_cast<uint32_t>(grid)), dim3(W * 64), 0, stream,
                        static_cast<const T *>(p.A), static_cast<const T *>(p.B), static_cast<T *>(p.C), p.M, p.N,
                        p.K, p.lda, p.ldb, p.ldc, static_cast<const T *>(p.bias), p.act);
     return hipGetLastError();
@@ -365,9 +368,13 @@ const Variant *variant_f32_skinny(int mb, int nb, int ks)
     // 64-column strips (256-byte rows of B) for M <= 16 when N is large:
     // more 32-column strips than CUs read HBM more slowly (1 x 16384 x 8192:
     // 4.8 TB/s, against 6.9 at 8192 columns); measured 1 x 16384 x 16384,
-    // 188.7 against 221.1 us; 16 x 16384 x 8192, 97.8 against 118.2.
-    static const Variant w1 = {"mmrelu_skinny<float,16x64,ks1>", MMRELU_DTYPE_F32, 16, 64, 16, kThreads, 1, 4,
-                               launch_skinny<float, 1, 4, 1, 2>, 2.3f};
+    // 188.7 against 221.1 us; 16 x 16384 x 8192, 97.8 against 118.2. Four
+    // waves, four streams of B rows per CU instead of eight, read these deep
+    // products faster (1 x 16384 x 16384: 167.7 against 190.1 us; 1 x 16384
+    // x 32768: 326.1 against 380.7; 16 x 16384 x 4096: 38.4 against 41.4;
+    // equal at 1 x 32768 x 8192 and 8 x 65536 x 4096).
+    static const Variant w1 = {"mmrelu_skinny<float,16x64,ks1,w4>", MMRELU_DTYPE_F32, 16, 64, 16, 4 * 64, 1, 4,
+                               launch_skinny<float, 1, 4, 1, 2, 4>, 2.3f};
     // 64-row bands of A for N <= 16 when M is large, for the same reason
     // (measured: 16384 x 16 x 8192, 122.6 against 150.4 us on 32-row bands;
     // 32768 x 16 x 4096, 110.9 against 117.0). bf16 gains nothing from it.
@@ -399,9 +406,12 @@ const Variant *variant_bf16_skinny(int mb, int nb, int ks)
     // 64-column strips for M <= 16 when N is large: whole 128-byte lines of B
     // per row (measured: 1 x 16384 x 16384, 120.5 against 136.1 us on 32-column
     // strips; 4 x 32768 x 4096, 44.5 against 49.5). At N = 8192 they leave
-    // half the CUs idle and tie with the 32-column strips.
-    static const Variant w1 = {"mmrelu_skinny<bf16,16x64,ks1>", MMRELU_DTYPE_BF16, 16, 64, 32, kThreads, 1, 8,
-                               launch_skinny<uint16_t, 1, 4, 1, 2>, 10.1f};
+    // half the CUs idle and tie with the 32-column strips. Four waves, four
+    // streams of B rows per CU instead of eight (1 x 16384 x 16384: 96.9
+    // against 120.2 us; 1 x 16384 x 32768: 189.9 against 223.0; 16 x 16384 x
+    // 16384: 106.5 against 114.0; within 2% elsewhere).
+    static const Variant w1 = {"mmrelu_skinny<bf16,16x64,ks1,w4>", MMRELU_DTYPE_BF16, 16, 64, 32, 4 * 64, 1, 8,
+                               launch_skinny<uint16_t, 1, 4, 1, 2, 4>, 10.1f};
     if (nb == 4 && mb == 4) return &sq;
     if (nb == 4 && mb == 1) return &w1;
     if (nb == 2 && ks == 1) return mb == 1 ? &m1 : mb == 2 ? &m2 : &m4;
