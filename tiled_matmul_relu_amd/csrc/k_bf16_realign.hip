@@ -121,12 +121,16 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     const uintptr_t a_addr = reinterpret_cast<uintptr_t>(A + static_cast<int64_t>(m0) * lda);
     const uintptr_t b_addr = reinterpret_cast<uintptr_t>(B + n0);
     const int a_mis = static_cast<int>((a_addr >> 1) & 1), b_mis = static_cast<int>((b_addr >> 1) & 1);
-    const rsrc_t ra = make_rsrc(reinterpret_cast<const void *>(a_addr & ~uintptr_t{3}),
-                                ((a_mis + static_cast<int64_t>(rows - 1) * lda + K) * 2 + 3) & ~int64_t{3});
+    // Byte ranges of the A resource and of the B resource of slab k0: up to
+    // the word that holds the operand's last element.
+    const int64_t a_range = ((a_mis + static_cast<int64_t>(rows - 1) * lda + K) * 2 + 3) & ~int64_t{3};
+    auto b_range = [&](int k0) {
+        return ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3};
+    };
+    const rsrc_t ra = make_rsrc(reinterpret_cast<const void *>(a_addr & ~uintptr_t{3}), a_range);
     auto b_rsrc = [&](int k0) __attribute__((always_inline)) {
         const uintptr_t base = (b_addr + static_cast<uintptr_t>(static_cast<int64_t>(k0) * ldb * 2)) & ~uintptr_t{3};
-        return make_rsrc(reinterpret_cast<const void *>(base),
-                         ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3});
+        return make_rsrc(reinterpret_cast<const void *>(base), b_range(k0));
     };
     // First word of row r's window (byte offset from the word base, k0 = 0),
     // and whether the row is late.
@@ -166,11 +170,6 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         if (b_late(sd - kTile)) side_v = b_word0(sd - kTile) + 512;
     }
     const bool side_b = wave == 4;
-    // Byte ranges of the A resource and of the B resource of slab k0.
-    const int64_t a_range = ((a_mis + static_cast<int64_t>(rows - 1) * lda + K) * 2 + 3) & ~int64_t{3};
-    auto b_range = [&](int k0) {
-        return ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3};
-    };
 
     const int nk = (K + kSlab - 1) / kSlab;
     // The per-lane copy offsets pass through an empty asm once per slab, so
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // Copy q of slab s (zero fills for slabs past K) into stage s % 4; 16-byte
     // copies q = 0, 1 (A), 2, 3 (B), 4 (side words); 4-byte copies q = 4c + d
     // for the 16-byte copy c < 4, and 16 (side words). (Selects, not
-    // branches.)
+    // branches, inside a copy.)
     constexpr int kCopiesWide = 5, kCopiesNarrow = 17;
     auto issue_copy = [&](auto wide_c, int q, int s, const rsrc_t &rb, const CopyPlan &cp)
                           __attribute__((always_inline)) {
