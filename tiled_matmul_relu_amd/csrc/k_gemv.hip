@@ -56,7 +56,8 @@ __device__ inline void load16(const T *p, float (&f)[16 / sizeof(T)])
 // read element by element with stride ldb.
 template <typename T, bool VEC, bool BVEC>
 __global__ __launch_bounds__(kGemvThreads) void mmrelu_gemv(const T *__restrict__ A, const T *__restrict__ B,
-                                                           T *__restrict__ C, int M, int N, int K, int64_t lda,
+                                                           T *__restrict__ C, int M, [[maybe_unused]] int N, int K,
+                                                           int64_t lda,
                                                            int64_t ldb, int64_t ldc, const T *__restrict__ bias,
                                                            int act)
 {

@@ -189,7 +189,8 @@ __device__ inline void merge(float &m, float &s, float m2, float s2)
 // Any N: two passes over the row, one workgroup per row. V = 1 takes any
 // layout; V = 16 / sizeof(T) needs N % V == 0 and 16-byte aligned rows.
 template <typename T, int V>
-__global__ __launch_bounds__(kRowThreads) void softmax_online(const T *__restrict__ X, T *Y, int64_t M, int64_t N,
+__global__ __launch_bounds__(kRowThreads) void softmax_online(const T *__restrict__ X, T *Y, [[maybe_unused]] int64_t M,
+                                                             int64_t N,
                                                              int64_t ldx, int64_t ldy)
 {
     __shared__ float red_m[4], red_s[4];
