@@ -266,10 +266,13 @@ def mfma_ceiling(da, db, steps, warmup, torch):
     return res
 
 
-def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="relu", bias=False):
+def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="relu", bias=False, cold=False):
     """Per-call HIP-event times (ms) of one workload: mean, median, P95, and
     the rates derived from the median. act/bias select the fused epilogue
-    (the default is relu(A·B))."""
+    (the default is relu(A·B)). With cold, the same calls are timed once more
+    with a 512 MiB scratch write before each (larger than the 256 MB
+    Infinity Cache and the 8 x 4 MB of L2), so every call starts with its
+    operands in HBM only; the write itself is outside the events."""
     a, b = datagen.make_inputs(cfg)
     da, db = to_device(a, torch), to_device(b, torch)
     dbias = None
@@ -318,7 +321,27 @@ def per_call_stats(cfg, steps, warmup, torch, mm, datagen, variant=None, act="re
             mm.mmrelu_plan_variant(kind, variant, cfg.M, cfg.N, cfg.K, cfg.lda, cfg.ldb, cfg.ldc))
     alg_bytes = cfg.elem_bytes * (cfg.M * cfg.K + cfg.K * cfg.N + cfg.M * cfg.N)
     tf = cfg.flops / (med * 1e-3) / 1e12
-    return {"workload": cfg.name, "act": act, "bias": bool(bias), "M": cfg.M, "N": cfg.N, "K": cfg.K, "lda": cfg.lda, "ldb": cfg.ldb, "ldc": cfg.ldc,
+    extra = {}
+    if cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        tc = []
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tc.append(e0.elapsed_time(e1))
+        del scratch
+        tc.sort()
+        cmed = tc[steps // 2] if steps % 2 else 0.5 * (tc[steps // 2 - 1] + tc[steps // 2])
+        extra["cold_cache"] = {"what": "per call, after a 512 MiB scratch write (operands in HBM only)",
+                               "mean_ms": round(sum(tc) / steps, 5), "median_ms": round(cmed, 5),
+                               "p95_ms": round(tc[min(steps - 1, int(math.ceil(0.95 * steps)) - 1)], 5),
+                               "tflops_median": round(cfg.flops / (cmed * 1e-3) / 1e12, 3),
+                               "alg_gbs_median": round(alg_bytes / (cmed * 1e-3) / 1e9, 1)}
+    return {**extra, "workload": cfg.name, "act": act, "bias": bool(bias), "M": cfg.M, "N": cfg.N, "K": cfg.K, "lda": cfg.lda, "ldb": cfg.ldb, "ldc": cfg.ldc,
             "dtype": cfg.dtype, "kernel": plan["name"], "grid": plan["grid"], "waves": plan["waves"],
             "idle_slots_last_wave": plan["idle_slots_last"], "steps": steps, "warmup": warmup,
             "mean_ms": round(mean, 5), "median_ms": round(med, 5), "p95_ms": round(p95, 5),
@@ -575,6 +598,9 @@ def main():
     ap.add_argument("--act", choices=["relu", "gelu_tanh", "none"], default="relu",
                     help="with --all-configs: the fused epilogue's activation")
     ap.add_argument("--bias", action="store_true", help="with --all-configs: add a per-column bias")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="with --all-configs: also time each call after a 512 MiB scratch write (cold L2 and "
+                         "Infinity Cache)")
     ap.add_argument("--traffic-command", default="", help="the profiling command, stored with --record-traffic")
     args = ap.parse_args()
 
@@ -588,7 +614,8 @@ def main():
         mm.load_library()
         for ident, cfg in sorted(datagen.CONFIGS.items()):
             print(json.dumps({"config": ident, **per_call_stats(cfg, args.steps, args.warmup, torch, mm, datagen,
-                                                                act=args.act, bias=args.bias)}), flush=True)
+                                                                act=args.act, bias=args.bias,
+                                                                cold=args.cold_cache)}), flush=True)
         return
 
     if args.sweep:
