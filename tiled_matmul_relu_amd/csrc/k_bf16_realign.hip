@@ -32,10 +32,12 @@
 // step kt every wave multiplies slab kt (fragments in registers), reads slab
 // kt+1's fragments, realigns slab kt+2 and issues the copies of slab kt+4
 // into the stage slab kt left; one barrier per step. Every wave both
-// multiplies and moves data, so its fragment reads queue behind the copies
-// and the realign in the LDS: this schedule reaches 0.18-0.30 of the bf16
-// peak, against about 0.6 for the ping-pong kernels, whose two wave groups
-// take the two roles in turn but need 16-byte aligned rows.
+// multiplies and moves data, and the time per step follows the number of
+// instructions each wave issues besides its MFMAs: the copies of inner slabs
+// (all but the last few) carry no per-lane tests, and only late rows are
+// realigned. This schedule reaches 0.21-0.36 of the bf16 peak, against about
+// 0.6 for the ping-pong kernels, whose two wave groups take the two roles in
+// turn but need 16-byte aligned rows.
 //
 // LDS stage (34 KB): A, 256 rows x 64 bytes, chunk c of row r at r*64 +
 // 16 (c ^ (r/4 % 4)); B, 32 rows x 512 bytes, chunk c of row k at k*512 +
@@ -128,10 +130,6 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         return ((b_mis + static_cast<int64_t>(K - 1 - k0) * ldb + N - n0) * 2 + 3) & ~int64_t{3};
     };
     const rsrc_t ra = make_rsrc(reinterpret_cast<const void *>(a_addr & ~uintptr_t{3}), a_range);
-    auto b_rsrc = [&](int k0) __attribute__((always_inline)) {
-        const uintptr_t base = (b_addr + static_cast<uintptr_t>(static_cast<int64_t>(k0) * ldb * 2)) & ~uintptr_t{3};
-        return make_rsrc(reinterpret_cast<const void *>(base), b_range(k0));
-    };
     // First word of row r's window (byte offset from the word base, k0 = 0),
     // and whether the row is late.
     auto a_word0 = [&](int r) { return static_cast<uint32_t>(((a_mis + static_cast<int64_t>(r) * lda) >> 1) * 4); };
@@ -143,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // any 4-byte boundary (buffer loads of a dword or more need only 4-byte
     // alignment), or, near the end of an operand, 4 bytes a lane: a 16-byte
     // copy that would straddle the end of its resource's range is never
-    // issued (see `risky`). Either way wave w fills the same LDS bytes.
+    // issued (see `copy_edge`). Either way wave w fills the same LDS bytes.
     //  A copy q (0, 1) of wave w fills rows 128q + 16w + l/4, stored chunk
     //  l%4 = the row's chunk l%4 ^ (l/16 % 4); row 128q + r's window starts
     //  256 q lda bytes after row r's. As four 4-byte copies d = 0..3, copy d
@@ -154,158 +152,210 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     //  16q + r's window starts 32 q ldb bytes after row r's. As four 4-byte
     //  copies, copy d fills half d%2 of row 16q + 2w + d/2: stored chunk
     //  16 (d%2) + l/4, word l%4.
-    const int ax_row0 = 16 * wave + (lane >> 2);
-    const uint32_t ax_v0 = a_word0(ax_row0) + 16 * ((lane & 3) ^ ((lane >> 4) & 3));
-    const int bx_row0 = 2 * wave + (lane >> 5);
-    const uint32_t bx_v0 = b_word0(bx_row0) + 16 * ((lane & 31) ^ swz_b(bx_row0));
-    const int an_row0 = 16 * wave + (lane >> 4);
-    const uint32_t an_v0 = a_word0(an_row0) + 4 * (lane & 3);
-    // Side words: wave w's block holds words 64w .. 64w+63; words 0-255 are A
-    // rows' (word 16 of the window), 256-287 B slab rows' (word 128).
-    const int sd = 64 * wave + lane;
-    uint32_t side_v = kOutOfRange;
-    if (sd < kTile) {
-        if (sd < rows && a_late(sd)) side_v = a_word0(sd) + 64;
-    } else if (sd < kTile + kSlab) {
-        if (b_late(sd - kTile)) side_v = b_word0(sd - kTile) + 512;
-    }
+    //  Side words: wave w's block holds words 64w .. 64w+63; words 0-255 are
+    //  A rows' (word 16 of the window), 256-287 B slab rows' (word 128).
     const bool side_b = wave == 4;
-
     const int nk = (K + kSlab - 1) / kSlab;
-    // The per-lane copy offsets pass through an empty asm once per slab, so
-    // the compiler derives the offsets (and the edge tests) anew for each
-    // slab instead of keeping them all live across the K loop.
-    struct CopyPlan {
-        uint32_t ax, bx, an, side;
-        int ax_row, an_row;
+    auto ax_row = [&](int l) __attribute__((always_inline)) { return 16 * wave + (l >> 2); };
+    auto ax_plan = [&](int l) __attribute__((always_inline)) { return a_word0(ax_row(l)) + 16 * ((l & 3) ^ ((l >> 4) & 3)); };
+    auto bx_row = [&](int l) __attribute__((always_inline)) { return 2 * wave + (l >> 5); };
+    auto bx_plan = [&](int l) __attribute__((always_inline)) { return b_word0(bx_row(l)) + 16 * ((l & 31) ^ swz_b(bx_row(l))); };
+    auto side_plan = [&](int l) __attribute__((always_inline)) {
+        // Both candidates are computed and one selected (a branch here let
+        // the compiler select between the addresses of lda and ldb, which
+        // put them in scratch memory).
+        const int sd = 64 * wave + l, kb = sd - kTile;
+        const uint32_t va = a_word0(sd) + 64, vb = b_word0(kb) + 512;
+        const bool ok_a = sd < kTile && sd < rows && a_late(sd);
+        const bool ok_b = sd >= kTile && kb < kSlab && b_late(kb);
+        return ok_a ? va : (ok_b ? vb : kOutOfRange);
     };
-    auto copy_plan = [&]() __attribute__((always_inline)) {
-        CopyPlan c{ax_v0, bx_v0, an_v0, side_v, ax_row0, an_row0};
-        asm volatile("" : "+v"(c.ax), "+v"(c.bx), "+v"(c.an), "+v"(c.side), "+v"(c.ax_row), "+v"(c.an_row));
-        return c;
+    // Inner slabs. Every 16-byte copy of a slab with k0 + 32 <= K ends
+    // inside A's range: row r's window ends at most (r lda + k0 + 32) * 2
+    // bytes past the base, and the range at ((rows-1) lda + K) * 2. Its B
+    // rows all lie inside K, and row k's window ends at most (k ldb + 256) *
+    // 2 bytes past the slab's base, against ((K-1-k0) ldb + N - n0) * 2 for
+    // the range: inside it whenever (K - 32 - k0) ldb >= 256 - (N - n0),
+    // which b_slack turns into a count of slabs. For such slabs the copies
+    // need no tests at all: the only per-lane condition left, rows past M,
+    // is folded into the A offsets once per tile.
+    const int b_slack = N - n0 >= kTile ? 0 : static_cast<int>((kTile - (N - n0) + ldb - 1) / ldb);
+    auto inner_slab = [&](int s) __attribute__((always_inline)) { return s * kSlab + kSlab + b_slack <= K; };
+    uint32_t in_ax0, in_ax1, in_bx, in_side;
+    {
+        const uint32_t a0 = ax_plan(lane);
+        in_ax0 = ax_row(lane) < rows ? a0 : kOutOfRange;
+        in_ax1 = ax_row(lane) + 128 < rows ? a0 + static_cast<uint32_t>(256 * lda) : kOutOfRange;
+        in_bx = bx_plan(lane);
+        in_side = side_plan(lane);
+    }
+    // Resource of B's slab at k0 = 32 s: the base moves by 64 ldb bytes a
+    // slab (a multiple of 4, so the word alignment below the row start is
+    // the same for every slab) and the range shrinks by as much.
+    const uintptr_t b_base0 = b_addr & ~uintptr_t{3};
+    const int64_t b_range0 = b_range(0);
+    auto b_rsrc_slab = [&](int s) __attribute__((always_inline)) {
+        const int64_t step = static_cast<int64_t>(s) * 64 * ldb;
+        return make_rsrc(reinterpret_cast<const void *>(b_base0 + static_cast<uintptr_t>(step)), b_range0 - step);
     };
-    // Whether some 16-byte copy of this wave for slab s would straddle the
-    // end of its resource's range (the same for the whole wave). Such a slab
-    // is copied 4 bytes a lane: every 4-byte word is then wholly in range or
-    // wholly out, and no byte past an operand's last word is read.
-    auto risky = [&](int s, const CopyPlan &cp) __attribute__((always_inline)) {
+    // Copies of an inner slab (five per wave: A, A, B, B, side words).
+    auto copy_inner = [&](int s, rsrc_t rb) __attribute__((always_inline)) {
         const int k0 = s * kSlab;
+        const uint32_t st = lds0 + (s & (kStages - 1)) * kStageBytes;
+        load_to_lds<16>(ra, st + wave * 1024, in_ax0 + 2 * k0);
+        load_to_lds<16>(ra, st + (8 + wave) * 1024, in_ax1 + 2 * k0);
+        load_to_lds<16>(rb, st + kABytes + wave * 1024, in_bx);
+        load_to_lds<16>(rb, st + kABytes + (8 + wave) * 1024, in_bx + static_cast<uint32_t>(32 * ldb));
+        load_to_lds<4>(side_b ? rb : ra, st + kSideA + wave * 256, side_b ? in_side : in_side + 2 * k0);
+    };
+    // Copies of an edge slab (the last slabs, and slabs past K, which copy
+    // zeros): every copy tested against M and K, and the whole slab copied
+    // 4 bytes a lane if one of the wave's 16-byte copies would straddle the
+    // end of its range (every 4-byte word is wholly in range or wholly out).
+    // The plan is derived from the lane id again here, through an asm the
+    // compiler cannot see through, so none of it stays live across the loop.
+    constexpr int kCopiesWide = 5, kCopiesNarrow = 17;
+    auto copy_edge = [&](int s, rsrc_t rb) __attribute__((always_inline)) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int ar = ax_row(l), br = bx_row(l);
+        const uint32_t ax = ax_plan(l), bx = bx_plan(l), side = side_plan(l);
+        const bool live = s < nk;
+        const int k0 = s * kSlab;
+        const uint32_t st = lds0 + (s & (kStages - 1)) * kStageBytes;
         const int64_t rb_end = b_range(k0);
         bool r = false;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int64_t oa = static_cast<int64_t>(cp.ax) + 256 * q * lda + 2 * k0;
-            r |= cp.ax_row + 128 * q < rows && oa < a_range && oa + 16 > a_range;
-            const int64_t ob = static_cast<int64_t>(cp.bx) + 32 * q * ldb;
-            r |= k0 + bx_row0 + 16 * q < K && ob < rb_end && ob + 16 > rb_end;
+            const int64_t oa = static_cast<int64_t>(ax) + 256 * q * lda + 2 * k0;
+            r |= ar + 128 * q < rows && oa < a_range && oa + 16 > a_range;
+            const int64_t ob = static_cast<int64_t>(bx) + 32 * q * ldb;
+            r |= k0 + br + 16 * q < K && ob < rb_end && ob + 16 > rb_end;
         }
-        return s < nk && __builtin_amdgcn_ballot_w64(r) != 0;
-    };
-    // Copy q of slab s (zero fills for slabs past K) into stage s % 4; 16-byte
-    // copies q = 0, 1 (A), 2, 3 (B), 4 (side words); 4-byte copies q = 4c + d
-    // for the 16-byte copy c < 4, and 16 (side words). (Selects, not
-    // branches, inside a copy.)
-    constexpr int kCopiesWide = 5, kCopiesNarrow = 17;
-    auto issue_copy = [&](auto wide_c, int q, int s, const rsrc_t &rb, const CopyPlan &cp)
-                          __attribute__((always_inline)) {
-        constexpr bool kWide = decltype(wide_c)::value;
-        constexpr int kSide = kWide ? kCopiesWide - 1 : kCopiesNarrow - 1;
-        const bool live = s < nk;
-        const int k0 = s * kSlab;
-        const uint32_t st = lds0 + (s & (kStages - 1)) * kStageBytes;
-        if (q == kSide) {
-            const bool ok = live && cp.side != kOutOfRange && (!side_b || k0 + lane < K);
-            const uint32_t off = side_b ? cp.side : cp.side + static_cast<uint32_t>(2 * k0);
-            load_to_lds<4>(side_b ? rb : ra, st + kSideA + wave * 256, ok ? off : kOutOfRange);
-        } else if (kWide && q < 2) {
-            const bool ok = live && cp.ax_row + 128 * q < rows;
-            const uint32_t off = cp.ax + static_cast<uint32_t>(256 * q * lda + 2 * k0);
-            load_to_lds<16>(ra, st + (8 * q + wave) * 1024, ok ? off : kOutOfRange);
-        } else if (kWide) {
-            const int qq = q - 2;
-            const bool ok = live && k0 + bx_row0 + 16 * qq < K;
-            const uint32_t off = cp.bx + static_cast<uint32_t>(32 * qq * ldb);
-            load_to_lds<16>(rb, st + kABytes + (8 * qq + wave) * 1024, ok ? off : kOutOfRange);
-        } else if (q < 8) {
-            const int c = q >> 2, d = q & 3;
-            const bool ok = live && cp.an_row + 128 * c + 4 * d < rows;
-            const uint32_t off = cp.an + static_cast<uint32_t>((256 * c + 8 * d) * lda + 2 * k0) +
-                                 16 * (((lane >> 2) & 3) ^ d);
-            load_to_lds<4>(ra, st + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+        if (!(live && __builtin_amdgcn_ballot_w64(r) != 0)) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const bool ok = live && ar + 128 * q < rows;
+                const uint32_t off = ax + static_cast<uint32_t>(256 * q * lda + 2 * k0);
+                load_to_lds<16>(ra, st + (8 * q + wave) * 1024, ok ? off : kOutOfRange);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const bool ok = live && k0 + br + 16 * q < K;
+                const uint32_t off = bx + static_cast<uint32_t>(32 * q * ldb);
+                load_to_lds<16>(rb, st + kABytes + (8 * q + wave) * 1024, ok ? off : kOutOfRange);
+            }
         } else {
-            const int c = (q >> 2) - 2, d = q & 3;
-            const int row = 2 * wave + (d >> 1);                 // of the slab, less 16 c
-            const bool ok = live && k0 + row + 16 * c < K;
-            const uint32_t off = b_word0(row) + static_cast<uint32_t>(32 * c * ldb) +
-                                 16 * ((16 * (d & 1) + (lane >> 2)) ^ swz_b(row)) + 4 * (lane & 3);
-            load_to_lds<4>(rb, st + kABytes + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+            const int an_row = 16 * wave + (l >> 4);
+            const uint32_t an = a_word0(an_row) + 4 * (l & 3);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const bool ok = an_row + 128 * c + 4 * d < rows;
+                    const uint32_t off = an + static_cast<uint32_t>((256 * c + 8 * d) * lda + 2 * k0) +
+                                         16 * (((l >> 2) & 3) ^ d);
+                    load_to_lds<4>(ra, st + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+                }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int row = 2 * wave + (d >> 1);         // of the slab, less 16 c
+                    const bool ok = k0 + row + 16 * c < K;
+                    const uint32_t off = b_word0(row) + static_cast<uint32_t>(32 * c * ldb) +
+                                         16 * ((16 * (d & 1) + (l >> 2)) ^ swz_b(row)) + 4 * (l & 3);
+                    load_to_lds<4>(rb, st + kABytes + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
+                }
         }
+        const bool ok = live && side != kOutOfRange && (!side_b || k0 + l < K);
+        const uint32_t off = side_b ? side : side + static_cast<uint32_t>(2 * k0);
+        load_to_lds<4>(side_b ? rb : ra, st + kSideA + wave * 256, ok ? off : kOutOfRange);
     };
-    using Wide = std::integral_constant<bool, true>;
-    using Narrow = std::integral_constant<bool, false>;
     auto issue_slab = [&](int s) __attribute__((always_inline)) {
-        const rsrc_t rb = b_rsrc(s * kSlab);
-        const CopyPlan cp = copy_plan();
-        if (!risky(s, cp)) {
-#pragma unroll
-            for (int q = 0; q < kCopiesWide; ++q) issue_copy(Wide{}, q, s, rb, cp);
-        } else {
-#pragma unroll
-            for (int q = 0; q < kCopiesNarrow; ++q) issue_copy(Narrow{}, q, s, rb, cp);
-        }
+        const rsrc_t rb = b_rsrc_slab(s);
+        if (inner_slab(s)) copy_inner(s, rb);
+        else copy_edge(s, rb);
     };
 
-    // Realign plan. A: wave w rewrites rows 32w + 16j + l/4 (j = 0, 1),
-    // chunk l%4; the next chunk's first word, or the side word for the last
-    // chunk. B: rows 4w + 2j + l/32, chunk l%32. Row + 16 (A) and row + 2
-    // (B) have the same lateness (16 lda and 2 ldb are even).
-    const int ra_row = 32 * wave + (lane >> 2), ra_c = lane & 3;
-    const bool ra_late = a_late(ra_row);
+    // Realign plan: the late rows of a slab. With an odd leading dimension
+    // every other row is late, and one unit per lane covers them: A row
+    // 2 ((64w + l) / 4) + pa, chunk l%4, and B row 2 ((64w + l) / 32) + pb,
+    // chunk l%32 (pa, pb = 1 when row 0 is not late). With an even one
+    // every row is late or none is, and a lane has two units: A rows 32w +
+    // 16j + l/4 (j = 0, 1), B rows 4w + 2j + l/32. A unit joins its chunk
+    // with the next chunk's first word, or with the side word for the last
+    // chunk. A row's chunks sit in consecutive lanes of one wave, so every
+    // next word is read before any chunk of the row is rewritten.
+    const bool a_alt = (lda & 1) != 0, b_alt = (ldb & 1) != 0;
+    const int a_units = a_alt ? 1 : (a_late(0) ? 2 : 0);
+    const int b_units = b_alt ? 1 : (b_late(0) ? 2 : 0);
+    const int ra_row = a_alt ? 2 * ((64 * wave + lane) >> 2) + (a_late(0) ? 0 : 1) : 32 * wave + (lane >> 2);
+    const int ra_c = lane & 3;
     const uint32_t ra_main = a_byte(ra_row, ra_c);                                 // + 1024 j
     const uint32_t ra_next = ra_c < 3 ? a_byte(ra_row, ra_c + 1) : kSideA + 4 * ra_row;
     const uint32_t ra_step = ra_c < 3 ? 1024u : 64u;
-    const int rb_row = 4 * wave + (lane >> 5), rb_c = lane & 31;
-    const bool rb_late = b_late(rb_row);
+    const int rb_row = b_alt ? 2 * ((64 * wave + lane) >> 5) + (b_late(0) ? 0 : 1) : 4 * wave + (lane >> 5);
+    const int rb_c = lane & 31;
     uint32_t rb_main[2], rb_next[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         rb_main[j] = b_byte(rb_row + 2 * j, rb_c);
         rb_next[j] = rb_c < 31 ? b_byte(rb_row + 2 * j, rb_c + 1) : kSideB + 4 * (rb_row + 2 * j);
     }
-    // All reads of a wave's units come before its writes: a unit's next
-    // word belongs to a unit of the same wave, which is rewritten after.
     auto realign_a = [&](int s) __attribute__((always_inline)) {
         uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
         const int k0 = s * kSlab;
-        const bool tail = K - k0 < kSlab;
-        if (ra_late || tail) {
-            u32x4 v[2];
-            uint32_t x[2];
+        if (K - k0 >= kSlab) {                           // a whole slab: late rows only
+            if (a_units > 0) {
+                u32x4 v[2];
+                uint32_t x[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                v[j] = *reinterpret_cast<const u32x4 *>(st + ra_main + 1024 * j);
-                x[j] = *reinterpret_cast<const uint32_t *>(st + ra_next + ra_step * j);
-            }
+                for (int j = 0; j < 2; ++j)
+                    if (j < a_units) {
+                        v[j] = *reinterpret_cast<const u32x4 *>(st + ra_main + 1024 * j);
+                        x[j] = *reinterpret_cast<const uint32_t *>(st + ra_next + ra_step * j);
+                    }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (ra_late) v[j] = shift_down(v[j], x[j]);
-                if (tail) v[j] = keep_first(v[j], K - k0 - 8 * ra_c);
-                *reinterpret_cast<u32x4 *>(st + ra_main + 1024 * j) = v[j];
+                for (int j = 0; j < 2; ++j)
+                    if (j < a_units) *reinterpret_cast<u32x4 *>(st + ra_main + 1024 * j) = shift_down(v[j], x[j]);
             }
+            return;
+        }
+        // The slab that holds K's end (or lies past it): every row, late or
+        // not, has its elements past K zeroed; rows 32w + 16j + l/4, chunk
+        // l%4.
+        const int tr = 32 * wave + (lane >> 2);
+        const bool t_late = a_late(tr);
+        const uint32_t t_main = a_byte(tr, ra_c);
+        const uint32_t t_next = ra_c < 3 ? a_byte(tr, ra_c + 1) : kSideA + 4 * tr;
+        u32x4 v[2];
+        uint32_t x[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v[j] = *reinterpret_cast<const u32x4 *>(st + t_main + 1024 * j);
+            x[j] = *reinterpret_cast<const uint32_t *>(st + t_next + ra_step * j);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (t_late) v[j] = shift_down(v[j], x[j]);
+            *reinterpret_cast<u32x4 *>(st + t_main + 1024 * j) = keep_first(v[j], K - k0 - 8 * ra_c);
         }
     };
     auto realign_b = [&](int s) __attribute__((always_inline)) {
         uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
-        if (rb_late) {
+        if (b_units > 0) {
             u32x4 v[2];
             uint32_t x[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                v[j] = *reinterpret_cast<const u32x4 *>(st + rb_main[j]);
-                x[j] = *reinterpret_cast<const uint32_t *>(st + rb_next[j]);
-            }
+            for (int j = 0; j < 2; ++j)
+                if (j < b_units) {
+                    v[j] = *reinterpret_cast<const u32x4 *>(st + rb_main[j]);
+                    x[j] = *reinterpret_cast<const uint32_t *>(st + rb_next[j]);
+                }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4 *>(st + rb_main[j]) = shift_down(v[j], x[j]);
+            for (int j = 0; j < 2; ++j)
+                if (j < b_units) *reinterpret_cast<u32x4 *>(st + rb_main[j]) = shift_down(v[j], x[j]);
         }
     };
     auto realign = [&](int s) __attribute__((always_inline)) {
@@ -359,8 +409,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // after a slab of 4-byte copies, which is harmless), barrier; then eight
     // parts, one per A block i: the four MFMAs of block i of slab kt, the
     // read of block i of slab kt+1 and, in every other part, one B fragment
-    // of slab kt+1. After part 0 the copies of slab kt+4 (into slab kt's
-    // stage) are issued, after part 1 slab kt+2 is realigned, while the
+    // of slab kt+1. After part 0 slab kt+2 is realigned, after part 1 the
+    // copies of slab kt+4 (into slab kt's stage) are issued, while the
     // matrix cores work through the MFMAs issued so far. The fences keep each
     // part's MFMAs inside the part, ahead of the read that overwrites their
     // operand.
