@@ -85,6 +85,23 @@ __device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uin
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, %3 offen lds"
                      :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
 }
+// The same copy with no scalar offset (the inline constant 0 in its place,
+// which saves the scalar register move per copy).
+template <int Bytes>
+__device__ inline void load_to_lds_z(rsrc_t r, uint32_t lds, uint32_t voffset)
+{
+    static_assert(Bytes == 4 || Bytes == 16, "4- or 16-byte lanes");
+    lds = __builtin_amdgcn_readfirstlane(lds);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    asm("" : "+s"(lds));
+    if constexpr (Bytes == 16)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                     :: "v"(voffset), "s"(lds), "s"(r) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                     :: "v"(voffset), "s"(lds), "s"(r) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Store resource over [base, base + bytes) for the masked epilogue stores:

@@ -179,7 +179,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // which b_slack turns into a count of slabs. For such slabs the copies
     // need no tests at all: the only per-lane condition left, rows past M,
     // is folded into the A offsets once per tile.
-    const int b_slack = N - n0 >= kTile ? 0 : static_cast<int>((kTile - (N - n0) + ldb - 1) / ldb);
+    // (Per-tile values from 64-bit divisions are computed on the vector
+    // unit; readfirstlane puts them back in scalar registers.)
+    const int b_slack = __builtin_amdgcn_readfirstlane(
+        N - n0 >= kTile ? 0 : static_cast<int>((kTile - (N - n0) + ldb - 1) / ldb));
     auto inner_slab = [&](int s) __attribute__((always_inline)) { return s * kSlab + kSlab + b_slack <= K; };
     uint32_t in_ax0, in_ax1, in_bx, in_side;
     {
@@ -198,17 +201,37 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         const int64_t step = static_cast<int64_t>(s) * 64 * ldb;
         return make_rsrc(reinterpret_cast<const void *>(b_base0 + static_cast<uintptr_t>(step)), b_range0 - step);
     };
+    // The same for an inner slab, whose range is positive: kMaxRange until
+    // slab s_small, where it first falls below that, and from there on the
+    // low 32 bits of b_range0 - step (scalar 32-bit arithmetic only).
+    const int64_t b_over = b_range0 - kMaxRange;
+    const int s_small = __builtin_amdgcn_readfirstlane(
+        b_over <= 0 ? 0 : static_cast<int>((b_over + 64 * ldb - 1) / (64 * ldb)));
+    auto b_rsrc_inner = [&](int s) __attribute__((always_inline)) {
+        const uint64_t step = static_cast<uint64_t>(s) * 64 * static_cast<uint64_t>(ldb);
+        const uint64_t a = b_base0 + step;
+        const uint32_t range = s >= s_small ? static_cast<uint32_t>(b_range0) - static_cast<uint32_t>(step)
+                                            : static_cast<uint32_t>(kMaxRange);
+        rsrc_t r;
+        r[0] = static_cast<int32_t>(a);
+        r[1] = static_cast<int32_t>((a >> 32) & 0xFFFF);
+        r[2] = static_cast<int32_t>(range);
+        r[3] = static_cast<int32_t>(kBufferFormat);
+        return r;
+    };
     // Copies of an inner slab, five per wave: q = 0, 1 for A, 2, 3 for B,
     // 4 for the side words.
     auto copy_inner_q = [&](int s, int q, rsrc_t rb) __attribute__((always_inline)) {
         const int k0 = s * kSlab;
         const uint32_t st = lds0 + (s & (kStages - 1)) * kStageBytes;
-        if (q == 0) load_to_lds<16>(ra, st + wave * 1024, in_ax0 + 2 * k0);
-        if (q == 1) load_to_lds<16>(ra, st + (8 + wave) * 1024, in_ax1 + 2 * k0);
-        if (q == 2) load_to_lds<16>(rb, st + kABytes + wave * 1024, in_bx);
-        if (q == 3) load_to_lds<16>(rb, st + kABytes + (8 + wave) * 1024, in_bx + static_cast<uint32_t>(32 * ldb));
-        if (q == 4)
-            load_to_lds<4>(side_b ? rb : ra, st + kSideA + wave * 256, side_b ? in_side : in_side + 2 * k0);
+        if (q == 0) load_to_lds_z<16>(ra, st + wave * 1024, in_ax0 + 2 * k0);
+        if (q == 1) load_to_lds_z<16>(ra, st + (8 + wave) * 1024, in_ax1 + 2 * k0);
+        if (q == 2) load_to_lds_z<16>(rb, st + kABytes + wave * 1024, in_bx);
+        if (q == 3) load_to_lds_z<16>(rb, st + kABytes + (8 + wave) * 1024, in_bx + static_cast<uint32_t>(32 * ldb));
+        if (q == 4) {
+            if (side_b) load_to_lds_z<4>(rb, st + kSideA + wave * 256, in_side);
+            else load_to_lds_z<4>(ra, st + kSideA + wave * 256, in_side + 2 * k0);
+        }
     };
     auto copy_inner = [&](int s, rsrc_t rb) __attribute__((always_inline)) {
 #pragma unroll
@@ -309,6 +332,14 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         rb_main[j] = b_byte(rb_row + 2 * j, rb_c);
         rb_next[j] = rb_c < 31 ? b_byte(rb_row + 2 * j, rb_c + 1) : kSideB + 4 * (rb_row + 2 * j);
     }
+    // An operand without late rows has the main loop realign garbage in a
+    // spare part of the stage instead, so that its steps need no test: side
+    // words 288-511 are written (with zeros) by copies into the stage and
+    // read by nothing else.
+    const uint32_t dummy = kSideA + 4 * (kTile + kSlab) + 16 * (lane & 31);
+    static_assert(kSideA + 4 * (kTile + kSlab) + 16 * 32 <= kStageBytes, "spare side words");
+    const uint32_t ra_main_f = a_units > 0 ? ra_main : dummy, ra_next_f = a_units > 0 ? ra_next : dummy;
+    const uint32_t rb_main_f = b_units > 0 ? rb_main[0] : dummy, rb_next_f = b_units > 0 ? rb_next[0] : dummy;
     // The slab that holds K's end (or lies past it): every A row, late or
     // not, has its elements past K zeroed (rows 32w + 16j + l/4, chunk
     // l%4), and B's late rows are realigned as in any slab.
@@ -365,6 +396,20 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
         if (u < a_units) *reinterpret_cast<u32x4 *>(st + ra_main + 1024 * u) = shift_down(rl_va, rl_xa);
         if (u < b_units) *reinterpret_cast<u32x4 *>(st + rb_main[u]) = shift_down(rl_vb, rl_xb);
+    };
+    // The main loop's form: one unit of each operand, real or in the spare
+    // side words, with no test.
+    auto realign_read_f = [&](int s) __attribute__((always_inline)) {
+        const uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
+        rl_va = *reinterpret_cast<const u32x4 *>(st + ra_main_f);
+        rl_xa = *reinterpret_cast<const uint32_t *>(st + ra_next_f);
+        rl_vb = *reinterpret_cast<const u32x4 *>(st + rb_main_f);
+        rl_xb = *reinterpret_cast<const uint32_t *>(st + rb_next_f);
+    };
+    auto realign_write_f = [&](int s) __attribute__((always_inline)) {
+        uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
+        *reinterpret_cast<u32x4 *>(st + ra_main_f) = shift_down(rl_va, rl_xa);
+        *reinterpret_cast<u32x4 *>(st + rb_main_f) = shift_down(rl_vb, rl_xb);
     };
     // Two units per lane (even leading dimensions with every row late) are
     // done in full when first reached; one unit (odd ones) may be written
@@ -438,9 +483,15 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // (4097x3001x2049: 91.7 against 95.4 us with the copies together and the
     // realign in one part). The fences keep each part's MFMAs inside the
     // part, ahead of the read that overwrites their operand.
-    auto step = [&](int kt) __attribute__((always_inline)) {
-        const bool rl = kt + 2 < nk, rl_tail = rl && is_tail(kt + 2);
-        const bool inner = inner_slab(kt + 4);
+    // kFast: a step whose copies are of an inner slab and whose realign is
+    // of a whole slab with at most one late unit per lane (all steps but the
+    // last few, with an odd leading dimension or no late rows); its tests
+    // are then compile-time constants and its parts carry no branches.
+    auto step = [&](int kt, auto fast_c) __attribute__((always_inline)) {
+        constexpr bool kFast = decltype(fast_c)::value;
+        const bool rl = kFast || kt + 2 < nk, rl_tail = !kFast && rl && is_tail(kt + 2);
+        const bool inner = kFast || inner_slab(kt + 4);
+        const bool two = !kFast && rl_two;
         rsrc_t rb_step;
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<kCopiesWide>();
@@ -454,13 +505,18 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the LDS reads
             __builtin_amdgcn_sched_barrier(0);
-            if (i == 0 && rl) {
-                if (rl_tail || rl_two) realign(kt + 2);
-                else realign_read(kt + 2, 0);
+            if (kFast) {
+                if (i == 0) realign_read_f(kt + 2);
+                if (i == 1) realign_write_f(kt + 2);
+            } else {
+                if (i == 0 && rl) {
+                    if (rl_tail || two) realign(kt + 2);
+                    else realign_read(kt + 2, 0);
+                }
+                if (i == 1 && rl && !rl_tail && !two) realign_write(kt + 2, 0);
             }
-            if (i == 1 && rl && !rl_tail && !rl_two) realign_write(kt + 2, 0);
             if (inner) {
-                if (i == 1) rb_step = b_rsrc_slab(kt + 4);
+                if (i == 1) rb_step = kFast ? b_rsrc_inner(kt + 4) : b_rsrc_slab(kt + 4);
                 if (i >= 1 && i <= 5) copy_inner_q(kt + 4, i - 1, rb_step);
             } else if (i == 1) {
                 issue_slab(kt + 4);
@@ -484,7 +540,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         for (int j = 0; j < kNB; ++j) load_frag_b(fb[j], 0, j);
 #pragma unroll
         for (int i = 0; i < kMB; ++i) load_frag_a(0, i);
-        for (int kt = 0; kt + 1 < nk; ++kt) step(kt);
+        int kt = 0;
+        if (!rl_two)
+            for (; inner_slab(kt + 4); ++kt) step(kt, std::true_type{});
+        for (; kt + 1 < nk; ++kt) step(kt, std::false_type{});
 #pragma unroll
         for (int i = 0; i < kMB; ++i) mfma_row(i);
         wait_vmcnt<0>();                                  // the zero fills past K
