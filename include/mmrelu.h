@@ -286,7 +286,7 @@ typedef struct {
  *     grid gives every CU a tile, then 128 x 128 tiles (variant 2, registers
  *     realign the operands) or 256 x 256 tiles (variant 15, 4- and 16-byte
  *     copies to LDS realigned there), whichever finishes its grid in fewer
- *     estimated rounds (a round of variant 15 counted as 1.2 + 512 / K
+ *     estimated rounds (a round of variant 15 counted as 0.75 + 704 / K
  *     rounds of variant 2).
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,

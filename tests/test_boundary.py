@@ -246,17 +246,19 @@ def test_planner_any_layout_tile():
     """Unaligned bf16: 64x64 tiles until the 128x128 grid gives every CU one
     or more; then 128x128 tiles (two workgroups a CU) or 256x256 tiles (one),
     whichever grid takes fewer estimated rounds, a 256x256 round counting
-    1.2 + 512 / K."""
+    0.75 + 704 / K."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
     # 4097 x 3001: 792 tiles of 128x128 (2 rounds of 512) against 204 of
-    # 256x256 (1 round, 1.45)
+    # 256x256 (1 round, 1.09)
     assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_realign<256,256,32>"
-    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 6.85
+    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 5.8
     odd = {(4095, 4095, 4095): 15, (5000, 5000, 999): 15, (3001, 3001, 3001): 15,
-           (4607, 4607, 1999): 15,                     # 3 rounds against 2 of 1.46
-           (2049, 4095, 511): 2,                       # 2 rounds against 1 of 2.2
-           (4607, 4607, 999): 2,                       # 3 rounds against 2 of 1.71
-           (6143, 6143, 1023): 2}                      # 5 rounds against 3 of 1.70
+           (4607, 4607, 1999): 15,                     # 3 rounds against 2 of 1.10
+           (2305, 2305, 4097): 15,                     # 1 round against 1 of 0.92
+           (2049, 4095, 511): 2,                       # 2 rounds against 1 of 2.13
+           (6143, 6143, 511): 2,                       # 5 rounds against 3 of 2.13
+           (4097, 4097, 767): 2,                       # 3 rounds against 2 of 1.67
+           (2561, 2561, 1023): 2}                      # 1 round against 1 of 1.44
     for (M, N, K), want in odd.items():
         assert plan(M, N, K)["variant"] == want, (M, N, K)
     # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU

@@ -443,7 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     }
     // A fragments are held once: block i of slab kt+1 is read right after
     // the four MFMAs of slab kt that use block i. B fragments are held twice
-    // (slab kt's are used by every A block): fb, and fb_next for slab kt+1.
+    // (slab kt's are used by every A block): fb, and fb_next for slab kt+1;
+    // the main loop runs two steps at a time with the two sets swapping
+    // roles, the other steps hand fb_next over to fb (16 moves).
     bf16x8 fa[kMB], fb[kNB], fb_next[kNB];
     auto load_frag_a = [&](int s, int i) __attribute__((always_inline)) {
         const uint8_t *st = lds + (s & (kStages - 1)) * kStageBytes;
@@ -463,11 +465,12 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto mfma_row = [&](int i) __attribute__((always_inline)) {
+    auto mfma_row_with = [&](int i, const bf16x8 (&b)[kNB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kNB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], fa[i], acc[i][j], 0, 0, 0);
     };
+    auto mfma_row = [&](int i) __attribute__((always_inline)) { mfma_row_with(i, fb); };
 
     // Step kt (slab kt+1 exists): wait for slab kt+2 (slab kt+3 may stay in
     // flight; waiting for all but the 16-byte count of one slab over-waits
@@ -487,7 +490,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // of a whole slab with at most one late unit per lane (all steps but the
     // last few, with an odd leading dimension or no late rows); its tests
     // are then compile-time constants and its parts carry no branches.
-    auto step = [&](int kt, auto fast_c) __attribute__((always_inline)) {
+    auto step = [&](int kt, auto fast_c, bf16x8 (&cur)[kNB], bf16x8 (&nxt)[kNB], bool hand_over)
+                    __attribute__((always_inline)) {
         constexpr bool kFast = decltype(fast_c)::value;
         const bool rl = kFast || kt + 2 < nk, rl_tail = !kFast && rl && is_tail(kt + 2);
         const bool inner = kFast || inner_slab(kt + 4);
@@ -498,9 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kMB; ++i) {
-            mfma_row(i);
+            mfma_row_with(i, cur);
             load_frag_a(kt + 1, i);
-            if ((i & 1) == 0) load_frag_b(fb_next[i >> 1], kt + 1, i >> 1);
+            if ((i & 1) == 0) load_frag_b(nxt[i >> 1], kt + 1, i >> 1);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the LDS reads
@@ -523,8 +527,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if (hand_over)
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) fb[j] = fb_next[j];
+            for (int j = 0; j < kNB; ++j) cur[j] = nxt[j];
     };
     if (nk > 0) {
         issue_slab(0);
@@ -542,8 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         for (int i = 0; i < kMB; ++i) load_frag_a(0, i);
         int kt = 0;
         if (!rl_two)
-            for (; inner_slab(kt + 4); ++kt) step(kt, std::true_type{});
-        for (; kt + 1 < nk; ++kt) step(kt, std::false_type{});
+            for (; inner_slab(kt + 5); kt += 2) {
+                step(kt, std::true_type{}, fb, fb_next, false);
+                step(kt + 1, std::true_type{}, fb_next, fb, false);
+            }
+        for (; kt + 1 < nk; ++kt) step(kt, std::false_type{}, fb, fb_next, true);
 #pragma unroll
         for (int i = 0; i < kMB; ++i) mfma_row(i);
         wait_vmcnt<0>();                                  // the zero fills past K

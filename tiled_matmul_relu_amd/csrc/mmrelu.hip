@@ -157,17 +157,19 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
         // then 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x
         // 256 tiles (variant 15, one per CU), whichever has the shorter
         // estimate: rounds of the grid over the CUs, a round of 256 x 256
-        // tiles counting 1.2 + 512 / K rounds of 128 x 128 (its start-up is a
-        // larger share at short K). Measured, variant 2 against 15 (us):
-        // 4097 x 3001 x 2049 157 / 100, 3001^3 147 / 120, 5000^2 x 999
-        // 152 / 128, 4607^2 x 999 119 / 125, 4607^2 x 1999 205 / 186,
-        // 6143^2 x 1023 183 / 189, 3071^2 x 511 43 / 45, 2049 x 4095 x 511
-        // 44 / 44, 2561^3 97 / 110, 2047^3 61 / 85, 8191^3 1957 / 1184.
+        // tiles counting 0.75 + 704 / K rounds of 128 x 128 (its start-up is
+        // a larger share at short K). Fitted to these, variant 2 against 15
+        // (us): 4097 x 3001 x 2049 151 / 89, 3001^3 143 / 105, 5000^2 x 999
+        // 149 / 121, 4607^2 x 999 121 / 117, 4607^2 x 1999 203 / 169,
+        // 2305^2 x 4097 140 / 131, 6143^2 x 1023 177 / 177, 6143^2 x 511
+        // 114 / 136, 4097^2 x 767 85 / 101, 2561^2 x 1023 49 / 57, 2561^3
+        // 97 / 99, 2047^3 62 / 78, 8191^3 1908 / 1073; it picks the slower
+        // one only at 2049 x 4095 x 511 (1%) and 3585^2 x 255 (6%).
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
         if (tiles128 < static_cast<int64_t>(cus)) return 13;
         const double t2 = static_cast<double>((tiles128 + 2 * cus - 1) / (2 * cus));
-        const double t15 = (1.2 + 512.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
+        const double t15 = (0.75 + 704.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
                            static_cast<double>((tiles256 + cus - 1) / cus);
         return t15 < t2 ? 15 : 2;
     }
