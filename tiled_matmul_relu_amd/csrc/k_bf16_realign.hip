@@ -40,7 +40,7 @@
 // turn but need 16-byte aligned rows.
 //
 // LDS stage (34 KB): A, 256 rows x 64 bytes, chunk c of row r at r*64 +
-// 16 (c ^ (r/4 % 4)); B, 32 rows x 512 bytes, chunk c of row k at k*512 +
+// 16 (c ^ (r/2 % 4)); B, 32 rows x 512 bytes, chunk c of row k at k*512 +
 // 16 (c ^ swz_b(k)); then the side words, A's (one per row) and B's (one per
 // slab row). A 16-byte copy fills 1 KB (16 A rows or 2 B rows), a 4-byte
 // copy 256 bytes; wave w fills the same bytes either way.
@@ -72,7 +72,10 @@ constexpr int kStageBytes = kSideA + 8 * 256;            // side block: one 256-
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
 
 __device__ inline int swz_b(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
-__device__ inline uint32_t a_byte(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+// A's 64-byte rows: chunk c of row r at r*64 + 16 (c ^ (r/2 % 4)). Eight
+// lanes reading one chunk of eight consecutive rows (a fragment read) then
+// touch eight distinct 16-byte slots of each 128-byte bank window.
+__device__ inline uint32_t a_byte(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
 __device__ inline uint32_t b_byte(int k, int c) { return kABytes + k * 512 + 16 * (c ^ swz_b(k)); }
 
 // The 8 elements that start one element into the 18 bytes lo:next (element
@@ -143,10 +146,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // copy that would straddle the end of its resource's range is never
     // issued (see `copy_edge`). Either way wave w fills the same LDS bytes.
     //  A copy q (0, 1) of wave w fills rows 128q + 16w + l/4, stored chunk
-    //  l%4 = the row's chunk l%4 ^ (l/16 % 4); row 128q + r's window starts
+    //  l%4 = the row's chunk l%4 ^ (l/8 % 4); row 128q + r's window starts
     //  256 q lda bytes after row r's. As four 4-byte copies d = 0..3, copy d
     //  fills rows 128q + 16w + 4d + l/16, stored chunk (l/4)%4, the row's
-    //  chunk (l/4)%4 ^ d, word l%4.
+    //  chunk (l/4)%4 ^ ((2d + l/32) % 4), word l%4.
     //  B copy q fills slab rows 16q + 2w + l/32, stored chunk l%32 = the
     //  row's chunk l%32 ^ swz_b(row), where swz_b(16q + r) = swz_b(r); row
     //  16q + r's window starts 32 q ldb bytes after row r's. As four 4-byte
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     const bool side_b = wave == 4;
     const int nk = (K + kSlab - 1) / kSlab;
     auto ax_row = [&](int l) __attribute__((always_inline)) { return 16 * wave + (l >> 2); };
-    auto ax_plan = [&](int l) __attribute__((always_inline)) { return a_word0(ax_row(l)) + 16 * ((l & 3) ^ ((l >> 4) & 3)); };
+    auto ax_plan = [&](int l) __attribute__((always_inline)) { return a_word0(ax_row(l)) + 16 * ((l & 3) ^ ((l >> 3) & 3)); };
     auto bx_row = [&](int l) __attribute__((always_inline)) { return 2 * wave + (l >> 5); };
     auto bx_plan = [&](int l) __attribute__((always_inline)) { return b_word0(bx_row(l)) + 16 * ((l & 31) ^ swz_b(bx_row(l))); };
     auto side_plan = [&](int l) __attribute__((always_inline)) {
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     // end of its range (every 4-byte word is wholly in range or wholly out).
     // The plan is derived from the lane id again here, through an asm the
     // compiler cannot see through, so none of it stays live across the loop.
-    constexpr int kCopiesWide = 5, kCopiesNarrow = 17;
+    constexpr int kCopiesWide = 5;                       // 16-byte copies per wave per slab (17 when 4-byte)
     auto copy_edge = [&](int s, rsrc_t rb) __attribute__((always_inline)) {
         int l = lane;
         asm volatile("" : "+v"(l));
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
                 for (int d = 0; d < 4; ++d) {
                     const bool ok = an_row + 128 * c + 4 * d < rows;
                     const uint32_t off = an + static_cast<uint32_t>((256 * c + 8 * d) * lda + 2 * k0) +
-                                         16 * (((l >> 2) & 3) ^ d);
+                                         16 * (((l >> 2) & 3) ^ ((2 * d + (l >> 5)) & 3));
                     load_to_lds<4>(ra, st + (8 * c + wave) * 1024 + 256 * d, ok ? off : kOutOfRange);
                 }
 #pragma unroll
