@@ -22,7 +22,8 @@
 //    fragments are one ds_read_b128 (A) and two ds_read_b64_tr_b16 (B).
 //  * One slab is loaded into registers while the previous one is
 //    multiplied; double-buffered LDS; bias, activation and one rounding to
-//    bf16 in the epilogue, with a store per element so any ldc works.
+//    bf16 in the epilogue, which stages the tile in LDS and stores whole
+//    rows with the widest stores each row's alignment allows.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -33,8 +34,6 @@ namespace mmrelu {
 namespace {
 
 constexpr int kAnyBK = 32, kAnyThreads = 256;
-
-__device__ inline float bf16f(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 
 // XOR applied to the 16-byte chunk index of B row k in LDS (BT/8 chunks per
 // row): the 16 lanes of a transposed read touch rows k .. k+3 and spread
@@ -244,25 +243,94 @@ __global__ __launch_bounds__(kAnyThreads, 2) void mmrelu_bf16_any(
         __syncthreads();
     }
 
-    // Lane (g, t) of block (i, j) holds C[row t][cols 4g .. 4g+3] of the block.
-    with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
-        constexpr int ACT = decltype(act_c)::value;
-#pragma unroll
-        for (int i = 0; i < NBLK; ++i) {
-            const int row = m0 + wm * (BT / 2) + i * 16 + t;
-            if (row >= M) continue;
+    // Epilogue, through LDS. Lane (g, t) of block (i, j) holds C[row t][cols
+    // 4g .. 4g+3] of the block; bias and activation on fp32 and one rounding
+    // to bf16, then the tile goes to LDS (both stages are free after the
+    // loop's last barrier) and each wave stores whole rows of it with the
+    // widest stores the row's alignment allows: a row of C may start on any
+    // 2-byte boundary, and element-wise stores scattered over sixteen rows
+    // cost far more than row-long ones.
+    // Tile layout: row r's 8-byte unit u (columns 4u .. 4u+3) at element
+    // r BT + 4 ((u + r) % (BT/4)): the sixteen rows of a fragment's lanes
+    // start on distinct units, and a row read by BT/4 lanes touches each
+    // unit once.
+    constexpr int kUnits = BT / 4;                        // 8-byte units per tile row
+    constexpr int kRowsPerPass = 64 / kUnits;             // rows one wave covers per store
+    static_assert(BT * BT <= 2 * kStage, "the output tile fits in the stages");
+    {
+        float bj[NBLK][4];
+        if (bias != nullptr) {
+            const __amdgpu_buffer_rsrc_t rbias = make_bias_rsrc(bias, n0, N, 2);
 #pragma unroll
             for (int j = 0; j < NBLK; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = n0 + wn * (BT / 2) + j * 16 + 4 * g + r;
-                    if (col >= N) continue;
-                    const float b = bias != nullptr ? bf16f(bias[col]) : 0.0f;
-                    const float o = activate<ACT>(acc[i][j][r] + b);
-                    C[static_cast<int64_t>(row) * ldc + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o));
-                }
+                for (int r = 0; r < 4; ++r) bj[j][r] = bias_bf16(rbias, wn * (BT / 2) + j * 16 + 4 * g + r);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bj[j][r] = 0.0f;
         }
-    });
+        with_activation(act, [&](auto act_c) __attribute__((always_inline)) {
+            constexpr int ACT = decltype(act_c)::value;
+#pragma unroll
+            for (int i = 0; i < NBLK; ++i) {
+                const int row = wm * (BT / 2) + i * 16 + t;
+#pragma unroll
+                for (int j = 0; j < NBLK; ++j) {
+                    const int u = wn * (BT / 8) + j * 4 + g;
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(activate<ACT>(acc[i][j][r] + bj[j][r]));
+                    *reinterpret_cast<u32x2 *>(lds + row * BT + 4 * ((u + row) & (kUnits - 1))) =
+                        __builtin_bit_cast(u32x2, o);
+                }
+            }
+        });
+    }
+    __syncthreads();
+    // Wave w stores rows w BT/4 .. (w+1) BT/4 - 1, kRowsPerPass rows a pass;
+    // lane l takes row l / kUnits of the pass, columns 4 (l % kUnits) .. +3.
+    // A row starting a (mod 4) elements past an 8-byte boundary takes one
+    // 8-byte store per lane (a = 0), two 4-byte ones (a = 2), or a 2-, a 4-
+    // and a 2-byte one (a odd); a lane with columns past N stores its
+    // elements one at a time, those past N not at all; rows past M store
+    // nothing (kOutOfRange plus a few bytes is still past every range).
+    const int rows = M - m0 < BT ? M - m0 : BT;
+    const int ncols = N - n0;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_store_rsrc(C + static_cast<int64_t>(m0) * ldc + n0, (static_cast<int64_t>(rows - 1) * ldc + ncols) * 2);
+    const int cu = lane & (kUnits - 1);
+    const bool full_lane = 4 * cu + 3 < ncols;
+    const int a0 = static_cast<int>(((reinterpret_cast<uintptr_t>(C) >> 1) + static_cast<uint64_t>(m0) * ldc + n0) & 3);
+    const int ld3 = static_cast<int>(ldc & 3);
+#pragma unroll 1
+    for (int p = 0; p < BT / 4 / kRowsPerPass; ++p) {
+        const int row = wave * (BT / 4) + p * kRowsPerPass + lane / kUnits;
+        if (wave * (BT / 4) + p * kRowsPerPass >= rows) break;
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(lds + row * BT + 4 * ((cu + row) & (kUnits - 1)));
+        const uint32_t off = row < rows ? static_cast<uint32_t>((row * ldc + 4 * cu) * 2) : kOutOfRange;
+        const int a = (a0 + row * ld3) & 3;
+        if (full_lane) {
+            if (a == 0) {
+                store_b64(rc, off, v);
+            } else if (a == 2) {
+                store_b32(rc, off, v[0]);
+                store_b32(rc, off + 4, v[1]);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[0]), rc, off, 0, 0);
+                store_b32(rc, off + 2, (v[0] >> 16) | (v[1] << 16));
+                __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[1] >> 16), rc, off + 6, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint16_t e = static_cast<uint16_t>((k < 2 ? v[0] : v[1]) >> (16 * (k & 1)));
+                __builtin_amdgcn_raw_buffer_store_b16(e, rc, row < rows && 4 * cu + k < ncols ? off + 2 * k : kOutOfRange,
+                                                      0, 0);
+            }
+        }
+    }
 }
 
 template <int BT>
