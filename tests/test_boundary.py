@@ -243,34 +243,37 @@ def test_planner_square_skinny_tile():
 
 
 def test_planner_any_layout_tile():
-    """Unaligned bf16: 64x64 tiles until the 128x128 grid gives every CU one
-    or more; then 128x128 tiles (two workgroups a CU) or 256x256 tiles (one),
-    whichever grid takes fewer estimated rounds, a 256x256 round counting
-    0.75 + 704 / K."""
+    """Unaligned bf16: 64x64 tiles until the 128x128 grid gives three CUs in
+    four a tile; then 128x128 tiles (two workgroups a CU) or 256x256 tiles
+    (one), whichever grid takes fewer estimated rounds, a 256x256 round
+    counting 0.9 + 224 / K."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
     # 4097 x 3001: 792 tiles of 128x128 (2 rounds of 512) against 204 of
-    # 256x256 (1 round, 1.09)
+    # 256x256 (1 round, 1.01)
     assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_realign<256,256,32>"
-    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 5.8
+    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 4.5
     odd = {(4095, 4095, 4095): 15, (5000, 5000, 999): 15, (3001, 3001, 3001): 15,
-           (4607, 4607, 1999): 15,                     # 3 rounds against 2 of 1.10
-           (2305, 2305, 4097): 15,                     # 1 round against 1 of 0.92
-           (2049, 4095, 511): 2,                       # 2 rounds against 1 of 2.13
-           (6143, 6143, 511): 2,                       # 5 rounds against 3 of 2.13
-           (4097, 4097, 767): 2,                       # 3 rounds against 2 of 1.67
-           (2561, 2561, 1023): 2}                      # 1 round against 1 of 1.44
+           (4607, 4607, 1999): 15,                     # 3 rounds against 2 of 1.01
+           (2305, 2305, 4097): 15,                     # 1 round against 1 of 0.95
+           (2049, 4095, 511): 15,                      # 2 rounds against 1 of 1.34
+           (6143, 6143, 511): 15,                      # 5 rounds against 3 of 1.34
+           (4097, 4097, 767): 15,                      # 3 rounds against 2 of 1.19
+           (3585, 3585, 255): 15,                      # 2 rounds against 1 of 1.78
+           (2561, 2561, 1023): 2,                      # 1 round against 1 of 1.12
+           (1793, 1793, 1023): 2,                      # 196 tiles of 128x128: 1 round
+           (1537, 1537, 1537): 13}                     # 169 tiles of 128x128, under 192
     for (M, N, K), want in odd.items():
         assert plan(M, N, K)["variant"] == want, (M, N, K)
-    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU
+    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU, against 1 round of 1.01
     p = plan(2047, 2047, 2047)
     assert p["name"] == "mmrelu_bf16_any<128,128,32>" and p["grid"] == 16 * 16
     p = plan(1001, 1001, 1001)
     assert p["name"] == "mmrelu_bf16_any<64,64,32>" and p["grid"] == 16 * 16
     # the threshold moves with the CU count: 1001^2 on 64 CUs takes 128x128
     assert plan(1001, 1001, 1001, cus=64)["name"] == "mmrelu_bf16_any<128,128,32>"
-    # just at the threshold: 16 x 16 = 256 tiles, and one tile row fewer
-    assert plan(2048, 2047, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
-    assert plan(2048 - 128, 2047, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
+    # just at the threshold: 12 x 16 = 192 tiles, and one tile row fewer
+    assert plan(1536, 2047, 1001)["name"] == "mmrelu_bf16_any<128,128,32>"
+    assert plan(1536 - 128, 2047, 1001)["name"] == "mmrelu_bf16_any<64,64,32>"
 
 
 def test_every_variant_plans():

@@ -152,24 +152,29 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     else if (fits) cand = bf16_aligned;
     else {
         // bf16, any layout, on the matrix cores: 64 x 64 tiles (variant 13)
-        // until the 128 x 128 grid gives every CU a tile, which keep more CUs
-        // busy (measured: 1001^3, 21.1 against 33.6 us for 128 x 128 tiles);
-        // then 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x
-        // 256 tiles (variant 15, one per CU), whichever has the shorter
-        // estimate: rounds of the grid over the CUs, a round of 256 x 256
-        // tiles counting 0.75 + 704 / K rounds of 128 x 128 (its start-up is
-        // a larger share at short K). Fitted to these, variant 2 against 15
-        // (us): 4097 x 3001 x 2049 151 / 89, 3001^3 143 / 105, 5000^2 x 999
-        // 149 / 121, 4607^2 x 999 121 / 117, 4607^2 x 1999 203 / 169,
-        // 2305^2 x 4097 140 / 131, 6143^2 x 1023 177 / 177, 6143^2 x 511
-        // 114 / 136, 4097^2 x 767 85 / 101, 2561^2 x 1023 49 / 57, 2561^3
-        // 97 / 99, 2047^3 62 / 78, 8191^3 1908 / 1073; it picks the slower
-        // one only at 2049 x 4095 x 511 (1%) and 3585^2 x 255 (6%).
+        // until the 128 x 128 grid gives three CUs in four a tile (more CUs
+        // busy; measured: 1001^3 20.5 against 31.6 us on 128 x 128 tiles,
+        // 1537^3 44.1 against 46.3, 1281^2 x 4097 86.7 against 108.0); then
+        // 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x 256
+        // tiles (variant 15, one per CU), whichever has the shorter estimate:
+        // rounds of the grid over the CUs, a round of 256 x 256 tiles
+        // counting 0.9 + 224 / K rounds of 128 x 128 (its start-up is a
+        // larger share at short K). Fitted to these, variant 2 against 15
+        // (us): 4097 x 3001 x 2049 148 / 77, 3001^3 141 / 95, 5000^2 x 999
+        // 123 / 88, 4607^2 x 999 106 / 88, 4607^2 x 1999 194 / 140, 2305^2 x
+        // 4097 141 / 117, 2049^2 x 4097 139 / 117, 6143^2 x 1023 160 / 134,
+        // 6143^2 x 511 94 / 90, 4097^2 x 767 74 / 73, 3585^2 x 255 31 / 26,
+        // 3071^2 x 511 35 / 32, 2561^3 98 / 84, 2561^2 x 1023 45 / 43,
+        // 1025 x 4097 x 1025 44 / 42, 513 x 8191 x 1001 43 / 41, 2047^3
+        // 60 / 67, 3073 x 1025 x 2049 58 / 67, 1793^2 x 1023 34 / 41, 8191^3
+        // 1962 / 1024; it picks the slower one at 2561^2 x 1023, 1025 x 4097
+        // x 1025 and 513 x 8191 x 1001 (4-5%), and at 2049^2 x 255 takes
+        // 128 x 128 tiles (17.7 us) where 64 x 64 ones take 16.6.
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
         const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (tiles128 < static_cast<int64_t>(cus)) return 13;
+        if (4 * tiles128 < 3 * static_cast<int64_t>(cus)) return 13;
         const double t2 = static_cast<double>((tiles128 + 2 * cus - 1) / (2 * cus));
-        const double t15 = (0.75 + 704.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
+        const double t15 = (0.9 + 224.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
                            static_cast<double>((tiles256 + cus - 1) / cus);
         return t15 < t2 ? 15 : 2;
     }
