@@ -86,7 +86,10 @@ __device__ inline void load_to_lds(rsrc_t r, uint32_t lds, uint32_t voffset, uin
                      :: "v"(voffset), "s"(lds), "s"(r), "s"(soffset) : "memory", "m0");
 }
 // The same copy with no scalar offset (the inline constant 0 in its place,
-// which saves the scalar register move per copy).
+// which saves the scalar register move per copy). The LDS address needs no
+// pinning to a register here: it is only moved into M0, which takes a
+// literal as well (an empty asm that pinned it made the compiler put a wait
+// state before every copy).
 template <int Bytes>
 __device__ inline void load_to_lds_z(rsrc_t r, uint32_t lds, uint32_t voffset)
 {
@@ -94,7 +97,6 @@ __device__ inline void load_to_lds_z(rsrc_t r, uint32_t lds, uint32_t voffset)
     lds = __builtin_amdgcn_readfirstlane(lds);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
-    asm("" : "+s"(lds));
     if constexpr (Bytes == 16)
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                      :: "v"(voffset), "s"(lds), "s"(r) : "memory", "m0");
