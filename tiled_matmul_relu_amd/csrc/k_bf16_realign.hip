@@ -26,8 +26,8 @@
 // Whether a row is late depends on the row only (slabs start at multiples of
 // 32 elements, so k0 * ld is even): the plan is made once per tile.
 //
-// Tile 256 x 256 per workgroup of eight waves (2 x 4), each a 128 x 64
-// sub-tile of 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128 fp32
+// Tile BM x 256 per workgroup of eight waves (2 x 4), each a BM/2 x 64
+// sub-tile of BM/32 x 4 blocks of v_mfma_f32_16x16x32_bf16 (up to 128 fp32
 // accumulators per lane); K in slabs of 32 in a ring of four LDS stages. In
 // step kt every wave multiplies slab kt (fragments in registers), reads slab
 // kt+1's fragments, realigns slab kt+2 and issues the copies of slab kt+4
@@ -38,6 +38,11 @@
 // realigned. This schedule reaches 0.21-0.36 of the bf16 peak, against about
 // 0.6 for the ping-pong kernels, whose two wave groups take the two roles in
 // turn but need 16-byte aligned rows.
+//
+// BM is 256, 224, 192 or 160: the shorter tiles give shapes whose 256-row
+// grid would leave CUs idle more tiles of less work each (4097 x 3001: 204
+// tiles of 256 rows, 228 of 224). Copies and realign always cover 256 rows;
+// rows past BM belong to the next tile and are staged but not multiplied.
 //
 // LDS stage (34 KB): A, 256 rows x 64 bytes, chunk c of row r at r*64 +
 // 16 (c ^ (r/2 % 4)); B, 32 rows x 512 bytes, chunk c of row k at k*512 +
@@ -51,8 +56,9 @@
 // hold whatever follows in memory and only reach outputs past N, which are
 // never stored. Each resource ends at the word that holds the operand's last
 // element, and a 4-byte word never crosses a page, so the bytes read around
-// an operand are always mapped. Outputs are stored one element at a time, so
-// any ldc works.
+// an operand are always mapped. The output tile is staged in LDS and stored
+// in whole rows, each with the widest stores its alignment allows, so any
+// ldc works.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -63,7 +69,7 @@ namespace mmrelu {
 namespace {
 
 constexpr int kTile = 256, kSlab = 32, kThreads = 512, kStages = 4;
-constexpr int kMB = 8, kNB = 4;                          // MFMA blocks per wave: 128 rows x 64 columns
+constexpr int kNB = 4;                                   // MFMA column blocks per wave: 64 columns
 constexpr int kABytes = kTile * kSlab * 2;               // A part of a stage
 constexpr int kBBytes = kSlab * kTile * 2;               // B part
 constexpr int kSideA = kABytes + kBBytes;                // A's side words, one per tile row
@@ -102,11 +108,14 @@ __device__ inline u32x4 keep_first(u32x4 x, int v)
     return x;
 }
 
+template <int BM>
 __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, uint16_t *__restrict__ C, int M, int N, int K,
     int64_t lda, int64_t ldb, int64_t ldc, int tiles_m, int tiles_n, int group_m, const uint16_t *__restrict__ bias,
     int act)
 {
+    static_assert(BM % 32 == 0 && BM >= 160 && BM <= kTile, "tile rows");
+    constexpr int kMB = BM / 32;                          // MFMA row blocks per wave: BM/2 rows
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
     const int lane = threadIdx.x & 63;
@@ -116,8 +125,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
 
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * kTile, n0 = tn * kTile;
-    const int rows = M - m0;                              // valid tile rows (may exceed 256)
+    const int m0 = tm * BM, n0 = tn * kTile;
+    const int rows = M - m0;                              // rows of A and C from m0 on (may exceed BM)
     const uint32_t lds0 = lds_address(lds);
 
     // Word bases. Row r of the tile starts a_mis + r lda elements past A's
@@ -431,10 +440,10 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         }
     };
 
-    // Fragment reads. A block i: rows wm*128 + 16i + t, chunk g; B block j:
+    // Fragment reads. A block i: rows wm*BM/2 + 16i + t, chunk g; B block j:
     // lane t of group g addresses slab row 8g + t/4 (+4 for the second
     // half) at columns wn*64 + 16j + 4(t%4) .. +3.
-    const uint32_t a_frag = a_byte(wm * 128 + t, g);                              // + 1024 i
+    const uint32_t a_frag = a_byte(wm * (BM / 2) + t, g);                         // + 1024 i
     uint32_t b_frag[kNB];
     {
         const int k_lane = 8 * g + (t >> 2);
@@ -507,7 +516,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         for (int i = 0; i < kMB; ++i) {
             mfma_row_with(i, cur);
             load_frag_a(kt + 1, i);
-            if ((i & 1) == 0) load_frag_b(nxt[i >> 1], kt + 1, i >> 1);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j)
+                if (i == j * kMB / kNB) load_frag_b(nxt[j], kt + 1, j);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the LDS reads
@@ -524,7 +535,9 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             }
             if (inner) {
                 if (i == 1) rb_step = kFast ? b_rsrc_inner(kt + 4) : b_rsrc_slab(kt + 4);
-                if (i >= 1 && i <= 5) copy_inner_q(kt + 4, i - 1, rb_step);
+#pragma unroll
+                for (int q = 0; q < 5; ++q)
+                    if (i == (1 + q < kMB - 1 ? 1 + q : kMB - 1)) copy_inner_q(kt + 4, q, rb_step);
             } else if (i == 1) {
                 issue_slab(kt + 4);
             }
@@ -590,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
             for (int i = 0; i < kMB; ++i) {
-                const int row = wm * 128 + i * 16 + t;
+                const int row = wm * (BM / 2) + i * 16 + t;
 #pragma unroll
                 for (int j = 0; j < kNB; ++j) {
                     const int u = wn * 16 + j * 4 + g;
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
         });
     }
     __syncthreads();
-    // Wave w stores rows 32w .. 32w+31 (those below M); lane l columns 4l ..
+    // Wave w stores rows w BM/8 .. (w+1) BM/8 - 1 (those below M); lane l columns 4l ..
     // 4l+3. A row starting a (mod 4) elements past an 8-byte boundary takes
     // one 8-byte store per lane (a = 0), two 4-byte ones (a = 2), or a 2-,
     // a 4- and a 2-byte one (a odd); a lane with columns past N stores its
@@ -616,8 +629,8 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
     const int a0 = static_cast<int>(((reinterpret_cast<uintptr_t>(C) >> 1) + static_cast<uint64_t>(m0) * ldc + n0) & 3);
     const int ld3 = static_cast<int>(ldc & 3);
 #pragma unroll 1
-    for (int rr = 0; rr < 32; ++rr) {
-        const int row = 32 * wave + rr;
+    for (int rr = 0; rr < BM / 8; ++rr) {
+        const int row = BM / 8 * wave + rr;
         if (row >= rows) break;
         const u32x2 v = *reinterpret_cast<const u32x2 *>(lds + row * 512 + 8 * ((lane + 4 * row) & 63));
         const uint32_t off = static_cast<uint32_t>((row * ldc + 4 * lane) * 2);
@@ -647,10 +660,11 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
 // XCD's range of tiles (tile_of).
 constexpr int kGroupM = 8;
 
+template <int BM>
 hipError_t launch_realign(const Problem &p, int64_t grid, hipStream_t stream)
 {
-    const int tiles_m = (p.M + kTile - 1) / kTile, tiles_n = (p.N + kTile - 1) / kTile;
-    hipLaunchKernelGGL(mmrelu_bf16_realign, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + kTile - 1) / kTile;
+    hipLaunchKernelGGL(mmrelu_bf16_realign<BM>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t *>(p.A), static_cast<const uint16_t *>(p.B),
                        static_cast<uint16_t *>(p.C), p.M, p.N, p.K, p.lda, p.ldb, p.ldc, tiles_m, tiles_n, kGroupM,
                        static_cast<const uint16_t *>(p.bias), p.act);
@@ -659,12 +673,18 @@ hipError_t launch_realign(const Problem &p, int64_t grid, hipStream_t stream)
 
 }  // namespace
 
-// 256 x 256 tiles, any layout.
-const Variant *variant_bf16_realign()
+// BM x 256 tiles (BM = 256, 224, 192 or 160), any layout.
+const Variant *variant_bf16_realign(int bm)
 {
-    static const Variant v = {"mmrelu_bf16_realign<256,256,32>", MMRELU_DTYPE_BF16, kTile, kTile, kSlab, kThreads,
-                              1, 0, launch_realign, 1.0f};
-    return &v;
+    static const Variant v256 = {"mmrelu_bf16_realign<256,256,32>", MMRELU_DTYPE_BF16, 256, kTile, kSlab, kThreads,
+                                 1, 0, launch_realign<256>, 1.0f};
+    static const Variant v224 = {"mmrelu_bf16_realign<224,256,32>", MMRELU_DTYPE_BF16, 224, kTile, kSlab, kThreads,
+                                 1, 0, launch_realign<224>, 1.0f};
+    static const Variant v192 = {"mmrelu_bf16_realign<192,256,32>", MMRELU_DTYPE_BF16, 192, kTile, kSlab, kThreads,
+                                 1, 0, launch_realign<192>, 1.0f};
+    static const Variant v160 = {"mmrelu_bf16_realign<160,256,32>", MMRELU_DTYPE_BF16, 160, kTile, kSlab, kThreads,
+                                 1, 0, launch_realign<160>, 1.0f};
+    return bm == 224 ? &v224 : bm == 192 ? &v192 : bm == 160 ? &v160 : &v256;
 }
 
 }  // namespace mmrelu

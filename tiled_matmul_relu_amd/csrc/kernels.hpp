@@ -58,8 +58,8 @@ const Variant *variant_bf16_skinny(int mb, int nb, int ks);
 // bf16 matrix-core kernel for any layout (k_bf16_any.hip).
 const Variant *variant_bf16_any(int bt);   // bt = 64 or 128
 // bf16 matrix-core kernel for any layout fed by 4-byte copies to LDS
-// (k_bf16_realign.hip): 256 x 256 tiles.
-const Variant *variant_bf16_realign();
+// (k_bf16_realign.hip): bm x 256 tiles, bm = 256, 224, 192 or 160.
+const Variant *variant_bf16_realign(int bm);
 // One wave per output (k_gemv.hip): matrix-vector products (N = 1), any layout.
 const Variant *variant_f32_gemv();
 const Variant *variant_bf16_gemv();

@@ -17,7 +17,7 @@ namespace {
 
 // Kernel tables in a fixed order (the variant index of the C-ABI).
 constexpr int kNumF32 = 15;
-constexpr int kNumBf16 = 16;
+constexpr int kNumBf16 = 19;
 // Both tables: 0 the plain kernel; 1 the large aligned tile and 2 the large
 // tile for any layout; 3 and 4 smaller tiles; 5 - 10 and 12 the skinny
 // tiles; 11 the matrix-vector kernel; 13 and 14 the rest; bf16 15 the
@@ -43,7 +43,9 @@ const Variant *const *bf16_table()
                                                variant_bf16_skinny(2, 1, 2), variant_bf16_skinny(2, 2, 2),
                                                variant_bf16_skinny(2, 4, 2), variant_bf16_gemv(),
                                                variant_bf16_skinny(4, 4, 2), variant_bf16_any(64),
-                                               variant_bf16_skinny(1, 4, 1), variant_bf16_realign()};
+                                               variant_bf16_skinny(1, 4, 1), variant_bf16_realign(256),
+                                               variant_bf16_realign(224), variant_bf16_realign(192),
+                                               variant_bf16_realign(160)};
     return t;
 }
 
