@@ -284,10 +284,10 @@ typedef struct {
  *     fp32 unaligned matrix-core kernels, or for bf16 the any-layout
  *     matrix-core kernels: 64 x 64 tiles (variant 13) until the 128 x 128
  *     grid gives three CUs in four a tile, then 128 x 128 tiles (variant 2,
- *     registers realign the operands) or 256 x 256 tiles (variant 15, 4- and
- *     16-byte copies to LDS realigned there), whichever finishes its grid in
- *     fewer estimated rounds (a round of variant 15 counted as 0.9 + 224 / K
- *     rounds of variant 2).
+ *     registers realign the operands) or BM x 256 tiles with BM = 256, 224,
+ *     192 or 160 (variants 15 - 18, 4- and 16-byte copies to LDS realigned
+ *     there), whichever has the smallest estimate: the busiest CU's tile
+ *     count times a fixed plus a per-k cost measured for each kernel.
  * The launch entry points make the same choice with the device's count. */
 int mmrelu_plan(int dtype, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, int32_t cus, mmrelu_plan_t *out);

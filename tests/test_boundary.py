@@ -244,27 +244,30 @@ def test_planner_square_skinny_tile():
 
 def test_planner_any_layout_tile():
     """Unaligned bf16: 64x64 tiles until the 128x128 grid gives three CUs in
-    four a tile; then 128x128 tiles (two workgroups a CU) or 256x256 tiles
-    (one), whichever grid takes fewer estimated rounds, a 256x256 round
-    counting 0.9 + 224 / K."""
+    four a tile; then 128x128 tiles (two workgroups a CU) or BM x 256 tiles
+    (one a CU, BM = 256, 224, 192, 160), whichever has the smallest busiest-
+    CU tile count times a + b K, with the fitted a (us) and b (us per k):
+    128x128 2.9 + 0.0167 K, 256 rows 16.6 + 0.0262 K, 224 rows 15.2 + 0.0243
+    K, 192 rows 14.0 + 0.0230 K, 160 rows 12.3 + 0.0230 K."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
-    # 4097 x 3001: 792 tiles of 128x128 (2 rounds of 512) against 204 of
-    # 256x256 (1 round, 1.01)
-    assert plan(4097, 3001, 2049)["name"] == "mmrelu_bf16_realign<256,256,32>"
-    assert plan(8191, 8191, 1001)["name"] == "mmrelu_bf16_realign<256,256,32>"   # 8 against 4.5
-    odd = {(4095, 4095, 4095): 15, (5000, 5000, 999): 15, (3001, 3001, 3001): 15,
-           (4607, 4607, 1999): 15,                     # 3 rounds against 2 of 1.01
-           (2305, 2305, 4097): 15,                     # 1 round against 1 of 0.95
-           (2049, 4095, 511): 15,                      # 2 rounds against 1 of 1.34
-           (6143, 6143, 511): 15,                      # 5 rounds against 3 of 1.34
-           (4097, 4097, 767): 15,                      # 3 rounds against 2 of 1.19
-           (3585, 3585, 255): 15,                      # 2 rounds against 1 of 1.78
-           (2561, 2561, 1023): 2,                      # 1 round against 1 of 1.12
-           (1793, 1793, 1023): 2,                      # 196 tiles of 128x128: 1 round
+    # 4097 x 3001: 204 tiles of 256 rows (1 per CU: 70.3) against 228 of 224
+    # rows (1: 65.0); 192 rows give 22 x 12 = 264 tiles, two on some CUs
+    p = plan(4097, 3001, 2049)
+    assert p["name"] == "mmrelu_bf16_realign<224,256,32>" and p["grid"] == 19 * 12
+    odd = {(4095, 4095, 4095): 15,                     # 256 tiles of 256 rows: one each
+           (8191, 8191, 8191): 15,                     # 4 per CU against 5, 6 and 7
+           (5000, 5000, 999): 16,                      # 2 per CU: 2 x 39.5 against 2 x 42.8
+           (4607, 4607, 999): 17,                      # 432 tiles of 192 rows: 2 x 37.0
+           (3001, 3001, 3001): 18,                     # 228 tiles of 160 rows, one each
+           (4097, 4097, 767): 18,                      # 442 of 160 rows: 2 x 29.9
+           (2561, 2561, 1023): 18,                     # 187 of 160 rows: 35.8 against 2 x 20.0
+           (1793, 1793, 1023): 2,                      # 196 tiles of 128x128, one each: 20.0
+           (2049, 2049, 255): 2,
            (1537, 1537, 1537): 13}                     # 169 tiles of 128x128, under 192
     for (M, N, K), want in odd.items():
         assert plan(M, N, K)["variant"] == want, (M, N, K)
-    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU, against 1 round of 1.01
+    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU: 37.1 against 59.4
+    # on 160 rows
     p = plan(2047, 2047, 2047)
     assert p["name"] == "mmrelu_bf16_any<128,128,32>" and p["grid"] == 16 * 16
     p = plan(1001, 1001, 1001)

@@ -634,9 +634,11 @@ def test_any_layout_even_leading_dims(offs, variant):
     assert np.all(np.isnan(datagen.bf16_bits_to_f32(pad))), "wrote outside C"
 
 
-# The any-layout 256 x 256 kernel (variant 15) copies a slab without edge
-# tests when every row of it lies inside K and none of its 16-byte copies can
-# reach the end of an operand's range; the last slabs take the tested path.
+# The any-layout BM x 256 kernels (variants 15 - 18, BM = 256, 224, 192, 160)
+# copy a slab without edge tests when every row of it lies inside K and none
+# of its 16-byte copies can reach the end of an operand's range; the last
+# slabs take the tested path. A tile shorter than 256 rows still stages 256
+# rows, the rest belonging to the next tile (or past M).
 # Where a tile's columns end within 256 of N, B's last rows can reach the end
 # of B's range from several slabs before K's end (more of them the smaller
 # ldb is), so those slabs are tested too. Odd leading dimensions, operands one
@@ -645,15 +647,16 @@ EDGE_SLABS = [(300, 40, 500, 501, 41, 43), (260, 300, 400, 401, 301, 300), (70, 
               (257, 259, 1000, 1001, 259, 261), (513, 600, 97, 99, 601, 603)]
 
 
+@pytest.mark.parametrize("variant", [15, 16, 17, 18])     # 256, 224, 192, 160 tile rows
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc", EDGE_SLABS, ids=[f"{s[0]}x{s[1]}x{s[2]}" for s in EDGE_SLABS])
-def test_any_layout_256_inner_and_edge_slabs(M, N, K, lda, ldb, ldc):
+def test_any_layout_realign_inner_and_edge_slabs(M, N, K, lda, ldb, ldc, variant):
     a = datagen.f32_to_bf16_bits(datagen.small_int_f32(4300 + M, M, K))
     b = datagen.f32_to_bf16_bits(datagen.small_int_f32(4400 + N, K, N))
     fa, pa = placed(a, 1, lda)
     fb, pb = placed(b, 1, ldb)
     fc, pc = placed(np.zeros((M, 0), np.uint16), 1, ldc)
-    print(f"inner/edge slabs {M}x{N}x{K} ld {lda},{ldb},{ldc}", flush=True)
-    rc = mm.mmrelu_bf16_variant(15, pa, pb, pc, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+    print(f"inner/edge slabs variant {variant} {M}x{N}x{K} ld {lda},{ldb},{ldc}", flush=True)
+    rc = mm.mmrelu_bf16_variant(variant, pa, pb, pc, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
     assert rc == mm.MMRELU_OK, mm.status_string(rc)
     torch.cuda.synchronize()
     whole = to_host(fc)

@@ -118,8 +118,8 @@ bool layout_fits(const Variant *v, int64_t N, int64_t K, int64_t lda, int64_t ld
 // full tiles of block_m x block_n outputs at the variant's measured relative
 // cost per output (wave quantisation of the grid over the CUs). bf16
 // layouts the 16-byte-vector kernels do not accept go to the any-layout
-// matrix-core kernels (variants 2, 13 and 15); the plain tiled kernel (variant 0) is
-// only reached through the _variant entry points.
+// matrix-core kernels (variants 2, 13 and 15 - 18); the plain tiled kernel
+// (variant 0) is only reached through the _variant entry points.
 // Pointers are taken as 16-byte aligned when null (planning without buffers).
 int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                        const void *A, const void *B, const void *C, int32_t cus)
@@ -155,30 +155,39 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     else {
         // bf16, any layout, on the matrix cores: 64 x 64 tiles (variant 13)
         // until the 128 x 128 grid gives three CUs in four a tile (more CUs
-        // busy; measured: 1001^3 20.5 against 31.6 us on 128 x 128 tiles,
-        // 1537^3 44.1 against 46.3, 1281^2 x 4097 86.7 against 108.0); then
-        // 128 x 128 tiles (variant 2, two workgroups per CU) or 256 x 256
-        // tiles (variant 15, one per CU), whichever has the shorter estimate:
-        // rounds of the grid over the CUs, a round of 256 x 256 tiles
-        // counting 0.9 + 224 / K rounds of 128 x 128 (its start-up is a
-        // larger share at short K). Fitted to these, variant 2 against 15
-        // (us): 4097 x 3001 x 2049 148 / 77, 3001^3 141 / 95, 5000^2 x 999
-        // 123 / 88, 4607^2 x 999 106 / 88, 4607^2 x 1999 194 / 140, 2305^2 x
-        // 4097 141 / 117, 2049^2 x 4097 139 / 117, 6143^2 x 1023 160 / 134,
-        // 6143^2 x 511 94 / 90, 4097^2 x 767 74 / 73, 3585^2 x 255 31 / 26,
-        // 3071^2 x 511 35 / 32, 2561^3 98 / 84, 2561^2 x 1023 45 / 43,
-        // 1025 x 4097 x 1025 44 / 42, 513 x 8191 x 1001 43 / 41, 2047^3
-        // 60 / 67, 3073 x 1025 x 2049 58 / 67, 1793^2 x 1023 34 / 41, 8191^3
-        // 1962 / 1024; it picks the slower one at 2561^2 x 1023, 1025 x 4097
-        // x 1025 and 513 x 8191 x 1001 (4-5%), and at 2049^2 x 255 takes
-        // 128 x 128 tiles (17.7 us) where 64 x 64 ones take 16.6.
+        // busy; measured: 1001^3 20.7 against 32.1 us on 128 x 128 tiles,
+        // 1537^3 43.2 against 46.5, 1281^2 x 4097 86.8 against 107.7). Then
+        // the candidate with the shortest estimate: 128 x 128 tiles (variant
+        // 2, two workgroups per CU) or BM x 256 tiles (variants 15 - 18, BM =
+        // 256, 224, 192, 160 rows, one workgroup per CU), estimated as the
+        // busiest CU's tile count times a + b K (us). a and b were fitted to
+        // back-to-back times of all six any-layout kernels on 30 shapes from
+        // 1001^3 to 8191^3 on one MI355X: a tile costs a fixed part (its
+        // start-up and epilogue) and a part per k, both smaller for fewer rows.
+        // The rule takes 0.8% more time than the best kernel of each shape
+        // summed over the 30 (the 256-row tiles alone: 6.5%); its worst
+        // picks are 3001^3 (160 rows, 88.1 us, where 192 rows take 81.7) and
+        // 2049^2 x 255 (128 x 128 tiles, 17.6 us against 16.3). Shorter tiles
+        // win where the 256-row grid leaves CUs idle or a round part-filled:
+        // 4607^2 x 999 75.6 us on 192 rows against 90.1 on 256, 4097^2 x 767
+        // 60.4 on 160 against 74.0; 8191^3 and 4095^3 keep 256 rows.
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
-        const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
         if (4 * tiles128 < 3 * static_cast<int64_t>(cus)) return 13;
-        const double t2 = static_cast<double>((tiles128 + 2 * cus - 1) / (2 * cus));
-        const double t15 = (0.9 + 224.0 / static_cast<double>(std::max<int64_t>(K, 1))) *
-                           static_cast<double>((tiles256 + cus - 1) / cus);
-        return t15 < t2 ? 15 : 2;
+        struct Candidate { int32_t variant; int64_t rows; double a, b; };
+        static const Candidate cands[] = {{2, 0, 2.9, 0.0167},    {15, 256, 16.6, 0.0262}, {16, 224, 15.2, 0.0243},
+                                          {17, 192, 14.0, 0.0230}, {18, 160, 12.3, 0.0230}};
+        int32_t pick = -1;
+        double pick_cost = 0.0;
+        for (const Candidate &c : cands) {
+            const int64_t tiles = c.rows == 0 ? tiles128 : ((M + c.rows - 1) / c.rows) * ((N + 255) / 256);
+            const double per_cu = static_cast<double>((tiles + cus - 1) / cus);
+            const double cost = per_cu * (c.a + c.b * static_cast<double>(K));
+            if (pick < 0 || cost < pick_cost) {
+                pick = c.variant;
+                pick_cost = cost;
+            }
+        }
+        return pick;
     }
     // Candidates: the dtype's two tile kernels, and with an aligned layout the
     // seven skinny tiles (variants 5 - 10 and 12), which split K over eight
