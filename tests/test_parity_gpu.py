@@ -322,11 +322,11 @@ def test_deterministic_repeats(dtype):
 
 # (dtype, variant, shape): the tile kernels on grids of several waves. bf16 1
 # and 3 are the ping-pong tiles (an LDS ring per operand, the two wave
-# groups swapping roles at every barrier), 4 the 128 x 128 tile, 15 the
-# any-layout 256 x 256 tile; fp32 1 the aligned 128 x 128 tile, 4 the
-# unaligned 64 x 64 tile.
+# groups swapping roles at every barrier), 4 the 128 x 128 tile, 15 and 18
+# the any-layout 256 x 256 and 160 x 256 tiles; fp32 1 the aligned 128 x 128
+# tile, 4 the unaligned 64 x 64 tile.
 DETERMINISM = [("bf16", 1, (4352, 4352, 520)), ("bf16", 3, (4352, 4352, 520)), ("bf16", 4, (4352, 4352, 520)),
-               ("bf16", 15, (4352, 4352, 520)),
+               ("bf16", 15, (4352, 4352, 520)), ("bf16", 18, (4352, 4352, 520)),
                ("f32", 1, (4352, 4352, 264)), ("f32", 4, (4352, 4352, 264))]
 
 
@@ -490,11 +490,12 @@ def run_fused(act, a, b, bias, M, N, K, variant):
 # and a grid of several bands of tile rows, with more tiles than XCDs and a
 # tile count that is not a multiple of eight (so both the regrouped ids and
 # the tail walk their bands). bf16: 1, 3 ping-pong tiles, 4 the 128 x 128
-# tile, 15 the any-layout 256 x 256 tile; fp32: 1, 2 the 128 x 128 tiles, 3,
-# 4 the 64 x 64 tiles.
+# tile, 2 and 13 the any-layout 128 x 128 and 64 x 64 tiles, 15 - 18 the
+# any-layout BM x 256 tiles; fp32: 1, 2 the 128 x 128 tiles, 3, 4 the 64 x 64
+# tiles.
 MULTIBAND = (2312, 2320, 200)
-TILE_KERNELS = [("bf16", 1), ("bf16", 3), ("bf16", 4), ("bf16", 15), ("f32", 1), ("f32", 2), ("f32", 3),
-                ("f32", 4)]
+TILE_KERNELS = [("bf16", 1), ("bf16", 3), ("bf16", 4), ("bf16", 2), ("bf16", 13), ("bf16", 15), ("bf16", 16),
+                ("bf16", 17), ("bf16", 18), ("f32", 1), ("f32", 2), ("f32", 3), ("f32", 4)]
 EPILOGUES = [("relu", False), ("gelu_tanh", True), ("none", True)]
 
 
@@ -554,8 +555,9 @@ def test_tile_kernels_multiband_exact_integers(dtype, variant):
 # 2313 x 2317 x 233 with lda = 235, ldb = 2319, ldc = 2321 (all odd) and A, B,
 # C starting 1, 2, 3 elements past a 16-byte boundary: rows of A and B start
 # on alternate halves of 4-byte words, the last slab holds 9 k, and the grid
-# has several bands of tiles. bf16 15 copies 4-byte words and realigns the
-# late rows in LDS; 2 and 13 realign in registers.
+# has several bands of tiles. bf16 15 - 18 copy 4-byte words and realign the
+# late rows in LDS (tiles of 256, 224, 192, 160 rows); 2 and 13 realign in
+# registers.
 ODD_SHAPE, ODD_LD, ODD_OFFS = (2313, 2317, 233), (235, 2319, 2321), (1, 2, 3)
 
 
@@ -578,7 +580,7 @@ def run_odd_layout(act, a, b, bias, variant):
     return c[:, :N]
 
 
-@pytest.mark.parametrize("variant", [15, 2, 13])
+@pytest.mark.parametrize("variant", [15, 16, 17, 18, 2, 13])
 def test_any_layout_odd_multiband_exact_integers(variant):
     """Small integers and an integer bias on the odd layout: bit-exact against
     the oracle rounded to nearest-even."""
@@ -591,7 +593,7 @@ def test_any_layout_odd_multiband_exact_integers(variant):
     np.testing.assert_array_equal(c, bf16_round_ref(oracle.fused("none", a, b, bias)))
 
 
-@pytest.mark.parametrize("variant", [15, 2])
+@pytest.mark.parametrize("variant", [15, 16, 17, 18, 2])
 @pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
 def test_any_layout_odd_multiband_normal(variant, act):
     """Normal inputs with a bias on the odd layout, every element against the

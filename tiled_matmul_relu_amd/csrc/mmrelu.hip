@@ -20,8 +20,8 @@ constexpr int kNumF32 = 15;
 constexpr int kNumBf16 = 19;
 // Both tables: 0 the plain kernel; 1 the large aligned tile and 2 the large
 // tile for any layout; 3 and 4 smaller tiles; 5 - 10 and 12 the skinny
-// tiles; 11 the matrix-vector kernel; 13 and 14 the rest; bf16 15 the
-// 256 x 256 tile for any layout.
+// tiles; 11 the matrix-vector kernel; 13 and 14 the rest; bf16 15 - 18 the
+// BM x 256 tiles for any layout (BM = 256, 224, 192, 160).
 const Variant *const *f32_table()
 {
     static const Variant *const t[kNumF32] = {variant_f32_simple(), variant_f32_mfma128(),
