@@ -486,15 +486,17 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
 
     // Step kt (slab kt+1 exists): wait for slab kt+2 (slab kt+3 may stay in
     // flight; waiting for all but the 16-byte count of one slab over-waits
-    // after a slab of 4-byte copies, which is harmless), barrier; then eight
-    // parts, one per A block i: the four MFMAs of block i of slab kt, the
-    // read of block i of slab kt+1 and, in every other part, one B fragment
-    // of slab kt+1. Between parts, while the matrix cores work through the
-    // MFMAs issued so far: after part 0 the late rows of slab kt+2 are read,
-    // after part 1 they are written back realigned (a single LDS round trip
-    // per part), and after parts 1-5 the five copies of slab kt+4 (into slab
-    // kt's stage) are issued one at a time (an edge slab's all after part
-    // 1). One at a time, a copy holds up the wave's next MFMAs for less
+    // after a slab of 4-byte copies, which is harmless), barrier; then
+    // BM/32 parts, one per A block i: the four MFMAs of block i of slab kt,
+    // the read of block i of slab kt+1 and, in four of the parts (every
+    // other one for 256 rows), one B fragment of slab kt+1. Between parts,
+    // while the matrix cores work through the MFMAs issued so far: after
+    // part 0 the late rows of slab kt+2 are read, after part 1 they are
+    // written back realigned (a single LDS round trip per part), and after
+    // parts 1-5 (the last part taking the rest when there are fewer) the
+    // five copies of slab kt+4 (into slab kt's stage) are issued one at a
+    // time (an edge slab's all after part 1). One at a time, a copy holds up
+    // the wave's next MFMAs for less
     // (4097x3001x2049: 91.7 against 95.4 us with the copies together and the
     // realign in one part). The fences keep each part's MFMAs inside the
     // part, ahead of the read that overwrites their operand.
