@@ -209,9 +209,9 @@ def placed(x: np.ndarray, off: int, ld: int):
 # (dtype, element offsets of A, B, C, variants). Only element alignment is
 # required of pointers; these start A, B and C 1..7 elements past a 16-byte
 # boundary, through the planner (None) and the kernels that accept such
-# layouts: bf16 2/13/15 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
+# layouts: bf16 2/13/15-18 (any layout) and 0 (plain); fp32 2/4 (unaligned tiles),
 # 11 (matrix-vector) and 0.
-MISALIGNED = [("bf16", (1, 3, 5), [None, 2, 13, 15, 0]), ("bf16", (7, 2, 0), [None, 2, 13, 15]),
+MISALIGNED = [("bf16", (1, 3, 5), [None, 2, 13, 15, 16, 17, 18, 0]), ("bf16", (7, 2, 0), [None, 2, 13, 15, 18]),
               ("bf16", (0, 0, 3), [None, 13, 15]), ("f32", (1, 2, 3), [None, 2, 4, 0]), ("f32", (3, 0, 1), [None, 2, 4])]
 
 
@@ -666,3 +666,24 @@ def test_any_layout_realign_inner_and_edge_slabs(M, N, K, lda, ldb, ldc, variant
     np.testing.assert_array_equal(c[:, :N], bf16_round_ref(oracle.mmrelu(a, b)))
     pad = np.concatenate([c[:, N:].ravel(), whole[:1], whole[1 + M * ldc:]])
     assert np.all(np.isnan(datagen.bf16_bits_to_f32(pad))), "wrote outside C"
+
+
+# The planner's tile height on odd-layout bf16 shapes, through the default
+# entry point (odd N and K keep the 16-byte kernels out): bit-exact against
+# the oracle on small integers, every element. On a 256-CU device the
+# planner gives these 224-, 160- and 192-row tiles.
+PLANNER_ODD = [((4097, 3001, 2049), "mmrelu_bf16_realign<224,256,32>"),
+               ((3001, 3001, 3001), "mmrelu_bf16_realign<160,256,32>"),
+               ((4607, 4607, 999), "mmrelu_bf16_realign<192,256,32>")]
+
+
+@pytest.mark.parametrize("shape,kernel", PLANNER_ODD, ids=[f"{s[0]}x{s[1]}x{s[2]}" for s, _ in PLANNER_ODD])
+def test_any_layout_planner_tile_heights_exact(shape, kernel):
+    M, N, K = shape
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert mm.mmrelu_plan(mm.DTYPE_BF16, M, N, K, K, N, N, cus=256)["name"] == kernel
+    a = datagen.f32_to_bf16_bits(datagen.small_int_f32(3900 + M, M, K))
+    b = datagen.f32_to_bf16_bits(datagen.small_int_f32(3950 + N, K, N))
+    print(f"planner tile height {M}x{N}x{K}", flush=True)
+    c, _ = run(a, b, M, N, K, K, N)
+    np.testing.assert_array_equal(c, bf16_round_ref(oracle.mmrelu(a, b)))
