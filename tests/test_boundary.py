@@ -247,26 +247,26 @@ def test_planner_any_layout_tile():
     four a tile; then 128x128 tiles (two workgroups a CU) or BM x 256 tiles
     (one a CU, BM = 256, 224, 192, 160), whichever has the smallest busiest-
     CU tile count times a + b K, with the fitted a (us) and b (us per k):
-    128x128 2.9 + 0.0167 K, 256 rows 16.6 + 0.0262 K, 224 rows 15.2 + 0.0243
-    K, 192 rows 14.0 + 0.0230 K, 160 rows 12.3 + 0.0230 K."""
+    128x128 3.1 + 0.0165 K, 256 rows 17.2 + 0.0243 K, 224 rows 15.6 + 0.0236
+    K, 192 rows 14.2 + 0.0225 K, 160 rows 12.3 + 0.0227 K."""
     plan = lambda m, n, k, cus=256: mm.mmrelu_plan(mm.DTYPE_BF16, m, n, k, k, n, n, cus=cus)
-    # 4097 x 3001: 204 tiles of 256 rows (1 per CU: 70.3) against 228 of 224
-    # rows (1: 65.0); 192 rows give 22 x 12 = 264 tiles, two on some CUs
+    # 4097 x 3001: 204 tiles of 256 rows (1 per CU: 67.0) against 228 of 224
+    # rows (1: 64.0); 192 rows give 22 x 12 = 264 tiles, two on some CUs
     p = plan(4097, 3001, 2049)
     assert p["name"] == "mmrelu_bf16_realign<224,256,32>" and p["grid"] == 19 * 12
     odd = {(4095, 4095, 4095): 15,                     # 256 tiles of 256 rows: one each
            (8191, 8191, 8191): 15,                     # 4 per CU against 5, 6 and 7
-           (5000, 5000, 999): 16,                      # 2 per CU: 2 x 39.5 against 2 x 42.8
-           (4607, 4607, 999): 17,                      # 432 tiles of 192 rows: 2 x 37.0
+           (5000, 5000, 999): 16,                      # 2 per CU: 2 x 39.2 against 2 x 41.5
+           (4607, 4607, 999): 17,                      # 432 tiles of 192 rows: 2 x 36.7
            (3001, 3001, 3001): 18,                     # 228 tiles of 160 rows, one each
-           (4097, 4097, 767): 18,                      # 442 of 160 rows: 2 x 29.9
-           (2561, 2561, 1023): 18,                     # 187 of 160 rows: 35.8 against 2 x 20.0
+           (4097, 4097, 767): 18,                      # 442 of 160 rows: 2 x 29.7
+           (2561, 2561, 1023): 18,                     # 187 of 160 rows: 35.5 against 2 x 20.0
            (1793, 1793, 1023): 2,                      # 196 tiles of 128x128, one each: 20.0
            (2049, 2049, 255): 2,
            (1537, 1537, 1537): 13}                     # 169 tiles of 128x128, under 192
     for (M, N, K), want in odd.items():
         assert plan(M, N, K)["variant"] == want, (M, N, K)
-    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU: 37.1 against 59.4
+    # 2047^2: 16 * 16 = 256 tiles of 128x128, one per CU: 36.9 against 58.8
     # on 160 rows
     p = plan(2047, 2047, 2047)
     assert p["name"] == "mmrelu_bf16_any<128,128,32>" and p["grid"] == 16 * 16

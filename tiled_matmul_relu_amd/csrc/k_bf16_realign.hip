@@ -486,20 +486,21 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
 
     // Step kt (slab kt+1 exists): wait for slab kt+2 (slab kt+3 may stay in
     // flight; waiting for all but the 16-byte count of one slab over-waits
-    // after a slab of 4-byte copies, which is harmless), barrier; then
-    // BM/32 parts, one per A block i: the four MFMAs of block i of slab kt,
-    // the read of block i of slab kt+1 and, in four of the parts (every
-    // other one for 256 rows), one B fragment of slab kt+1. Between parts,
-    // while the matrix cores work through the MFMAs issued so far: after
-    // part 0 the late rows of slab kt+2 are read, after part 1 they are
-    // written back realigned (a single LDS round trip per part), and after
-    // parts 1-5 (the last part taking the rest when there are fewer) the
-    // five copies of slab kt+4 (into slab kt's stage) are issued one at a
-    // time (an edge slab's all after part 1). One at a time, a copy holds up
-    // the wave's next MFMAs for less
-    // (4097x3001x2049: 91.7 against 95.4 us with the copies together and the
-    // realign in one part). The fences keep each part's MFMAs inside the
-    // part, ahead of the read that overwrites their operand.
+    // after a slab of 4-byte copies, which is harmless), barrier; then BM/32
+    // parts, one per A block i: the four MFMAs of block i of slab kt, the
+    // read of block i of slab kt+1 and, in four of the parts (every other
+    // one for 256 rows), one B fragment of slab kt+1. Between parts, while
+    // the matrix cores work through the MFMAs issued so far: after part 0
+    // the late rows of slab kt+2 are read; after part 2 (part 1 in the last
+    // steps) they are written back realigned, two parts of MFMAs hiding the
+    // read's latency (written after part 1: 4097x3001x2049 68.6 against
+    // 67.0 us, 3001^3 92.3 against 87.4); and after parts 1-5 (the last part
+    // taking the rest when there are fewer) the five copies of slab kt+4
+    // (into slab kt's stage) are issued one at a time (an edge slab's all
+    // after part 1). One at a time, a copy holds up the wave's next MFMAs
+    // for less (4097x3001x2049: 91.7 against 95.4 us with the copies
+    // together and the realign in one part). The fences keep each part's
+    // MFMAs inside the part, ahead of the read that overwrites their operand.
     // kFast: a step whose copies are of an inner slab and whose realign is
     // of a whole slab with at most one late unit per lane (all steps but the
     // last few, with an odd leading dimension or no late rows); its tests
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmrelu_bf16_realign(
             __builtin_amdgcn_sched_barrier(0);
             if (kFast) {
                 if (i == 0) realign_read_f(kt + 2);
-                if (i == 1) realign_write_f(kt + 2);
+                if (i == 2) realign_write_f(kt + 2);
             } else {
                 if (i == 0 && rl) {
                     if (rl_tail || two) realign(kt + 2);

@@ -155,8 +155,8 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
     else {
         // bf16, any layout, on the matrix cores: 64 x 64 tiles (variant 13)
         // until the 128 x 128 grid gives three CUs in four a tile (more CUs
-        // busy; measured: 1001^3 20.7 against 32.1 us on 128 x 128 tiles,
-        // 1537^3 43.2 against 46.5, 1281^2 x 4097 86.8 against 107.7). Then
+        // busy; measured: 1001^3 20.8 against 32.0 us on 128 x 128 tiles,
+        // 1537^3 43.2 against 45.9, 1281^2 x 4097 87.4 against 107.9). Then
         // the candidate with the shortest estimate: 128 x 128 tiles (variant
         // 2, two workgroups per CU) or BM x 256 tiles (variants 15 - 18, BM =
         // 256, 224, 192, 160 rows, one workgroup per CU), estimated as the
@@ -164,18 +164,19 @@ int32_t choose_variant(int dtype, int64_t M, int64_t N, int64_t K, int64_t lda, 
         // back-to-back times of all six any-layout kernels on 30 shapes from
         // 1001^3 to 8191^3 on one MI355X: a tile costs a fixed part (its
         // start-up and epilogue) and a part per k, both smaller for fewer rows.
-        // The rule takes 0.8% more time than the best kernel of each shape
-        // summed over the 30 (the 256-row tiles alone: 6.5%); its worst
-        // picks are 3001^3 (160 rows, 88.1 us, where 192 rows take 81.7) and
-        // 2049^2 x 255 (128 x 128 tiles, 17.6 us against 16.3). Shorter tiles
-        // win where the 256-row grid leaves CUs idle or a round part-filled:
-        // 4607^2 x 999 75.6 us on 192 rows against 90.1 on 256, 4097^2 x 767
-        // 60.4 on 160 against 74.0; 8191^3 and 4095^3 keep 256 rows.
+        // The rule takes 1.4% more time than the best kernel of each shape
+        // summed over the 30 (the 256-row tiles alone: 5.4%); its worst picks
+        // are 2049^2 x 255 (128 x 128 tiles, 17.6 us, where 64 x 64 ones take
+        // 16.0), 1999^2 x 8191 (128 x 128, 206.7 against 188.3 on 192 rows)
+        // and 3001^3 (160 rows, 88.1 against 80.6 on 192). Shorter tiles win
+        // where the 256-row grid leaves CUs idle or a round part-filled:
+        // 4607^2 x 999 76.0 us on 192 rows against 87.2 on 256, 4097^2 x 767
+        // 60.0 on 160 against 70.4; 8191^3 and 4095^3 keep 256 rows.
         const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
         if (4 * tiles128 < 3 * static_cast<int64_t>(cus)) return 13;
         struct Candidate { int32_t variant; int64_t rows; double a, b; };
-        static const Candidate cands[] = {{2, 0, 2.9, 0.0167},    {15, 256, 16.6, 0.0262}, {16, 224, 15.2, 0.0243},
-                                          {17, 192, 14.0, 0.0230}, {18, 160, 12.3, 0.0230}};
+        static const Candidate cands[] = {{2, 0, 3.1, 0.0165},    {15, 256, 17.2, 0.0243}, {16, 224, 15.6, 0.0236},
+                                          {17, 192, 14.2, 0.0225}, {18, 160, 12.3, 0.0227}};
         int32_t pick = -1;
         double pick_cost = 0.0;
         for (const Candidate &c : cands) {
