@@ -35,7 +35,7 @@
 // multiplies and moves data, and the time per step follows the number of
 // instructions each wave issues besides its MFMAs: the copies of inner slabs
 // (all but the last few) carry no per-lane tests, and only late rows are
-// realigned. This schedule reaches 0.21-0.36 of the bf16 peak, against about
+// realigned. This schedule reaches 0.24-0.45 of the bf16 peak, against about
 // 0.6 for the ping-pong kernels, whose two wave groups take the two roles in
 // turn but need 16-byte aligned rows.
 //
