@@ -32,10 +32,12 @@
 // step kt every wave multiplies slab kt (fragments in registers), reads slab
 // kt+1's fragments, realigns slab kt+2 and issues the copies of slab kt+4
 // into the stage slab kt left; one barrier per step. Every wave both
-// multiplies and moves data, and the time per step follows the number of
-// instructions each wave issues besides its MFMAs: the copies of inner slabs
-// (all but the last few) carry no per-lane tests, and only late rows are
-// realigned. This schedule reaches 0.24-0.45 of the bf16 peak, against about
+// multiplies and moves data, so a step lasts as long as each wave's own mix
+// of MFMAs, fragment reads, realign round trip and copy issue, which the two
+// waves of a SIMD, in the same phase, hide only in part: the copies of inner
+// slabs (all but the last few) carry no per-lane tests, only late rows are
+// realigned, and each realign's write comes two parts after its read. This
+// schedule reaches 0.24-0.45 of the bf16 peak, against about
 // 0.6 for the ping-pong kernels, whose two wave groups take the two roles in
 // turn but need 16-byte aligned rows.
 //
