@@ -5,6 +5,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 import tiled_matmul_relu_amd as mm
@@ -289,6 +290,36 @@ def test_every_variant_plans():
             assert p["variant"] == v and p["grid"] == p["tiles_m"] * p["tiles_n"] > 0
             names.add(p["name"])
         assert len(names) == n
+
+
+def test_planner_picks_a_kernel_that_accepts_the_layout():
+    """Seeded random shapes and leading dimensions, both dtypes, several CU
+    counts: the planned kernel is one whose layout contract the arguments
+    meet (16-byte-vector kernels need N, K and every leading dimension to be
+    multiples of 16 bytes; any-layout, matrix-vector and plain kernels take
+    anything), skinny tiles cover every row or column they are given, and
+    the plan's grid covers the output exactly once."""
+    rng = np.random.default_rng(20261202)
+    any_layout = ("simple", "unaligned", "gemv", "_any<", "_realign<")
+    for _ in range(3000):
+        dt = int(rng.integers(0, 2))
+        q = 4 if dt == mm.DTYPE_F32 else 8
+        aligned = rng.random() < 0.5
+        dims = []
+        for _d in range(3):
+            x = int(rng.choice([rng.integers(1, 65), rng.integers(1, 3000), rng.integers(1, 9000)]))
+            dims.append((x + q - 1) // q * q if aligned else x)
+        M, N, K = dims
+        pad = lambda v: v + (int(rng.integers(0, 3)) * q if aligned else int(rng.integers(0, 5)))
+        lda, ldb, ldc = pad(K), pad(N), pad(N)
+        cus = int(rng.choice([64, 80, 256, 304]))
+        p = mm.mmrelu_plan(dt, M, N, K, lda, ldb, ldc, cus=cus)
+        name = p["name"]
+        if not any(t in name for t in any_layout):
+            assert all(x % q == 0 for x in (N, K, lda, ldb, ldc)), (dt, M, N, K, lda, ldb, ldc, name)
+        assert p["tiles_m"] == -(-M // p["block_m"]) and p["tiles_n"] == -(-N // p["block_n"]), (M, N, p)
+        assert p["grid"] == p["tiles_m"] * p["tiles_n"]
+        assert p["variant"] != 0, "the plain kernel is only reached through the _variant entry points"
 
 
 def test_python_wrapper_rejects_bad_tensors():
