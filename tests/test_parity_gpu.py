@@ -687,3 +687,54 @@ def test_any_layout_planner_tile_heights_exact(shape, kernel):
     print(f"planner tile height {M}x{N}x{K}", flush=True)
     c, _ = run(a, b, M, N, K, K, N)
     np.testing.assert_array_equal(c, bf16_round_ref(oracle.mmrelu(a, b)))
+
+
+# Seeded random shapes, leading dimensions and element offsets through the
+# planner in both dtypes: whatever kernel it picks (tile, skinny, any-layout,
+# matrix-vector) must reproduce the oracle bit for bit on small integers, and
+# write nothing outside C.
+RANDOM_CASES = 36
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES))
+def test_planner_random_layouts_exact(case):
+    rng = np.random.default_rng(7000 + case)
+    dtype = "f32" if case % 2 == 0 else "bf16"
+    M, N, K = (int(rng.integers(1, 700)) for _ in range(3))
+    if case % 3 == 0:
+        # every third case meets the 16-byte kernels' contract (sizes, leading
+        # dimensions and 16-byte aligned pointers), half of those with few
+        # rows, so the tile and skinny kernels are reached too
+        q = 4 if dtype == "f32" else 8
+        M = int(rng.integers(1, 65)) if case % 6 == 0 else M
+        N, K = -(-N // q) * q, -(-K // q) * q
+        lda, ldb, ldc = (x + q * int(rng.integers(0, 3)) for x in (K, N, N))
+        offs = [0, 0, 0]
+    else:
+        lda, ldb, ldc = K + int(rng.integers(0, 9)), N + int(rng.integers(0, 9)), N + int(rng.integers(0, 9))
+        offs = [int(rng.integers(0, 8)) for _ in range(3)]
+    a = datagen.small_int_f32(7100 + case, M, K)
+    b = datagen.small_int_f32(7200 + case, K, N)
+    if dtype == "bf16":
+        a, b = datagen.f32_to_bf16_bits(a), datagen.f32_to_bf16_bits(b)
+    fa, pa = placed(a, offs[0], lda)
+    fb, pb = placed(b, offs[1], ldb)
+    fc, pc = placed(np.zeros((M, 0), a.dtype), offs[2], ldc)
+    kind = mm.DTYPE_F32 if dtype == "f32" else mm.DTYPE_BF16
+    name = mm.mmrelu_plan(kind, M, N, K, lda, ldb, ldc)["name"]
+    print(f"random layout case {case}: {dtype} {M}x{N}x{K} ld {lda},{ldb},{ldc} offs {offs} ({name})", flush=True)
+    args = (pa, pb, pc, M, N, K, lda, ldb, ldc, torch.cuda.current_stream().cuda_stream)
+    rc = mm.mmrelu_f32(*args) if dtype == "f32" else mm.mmrelu_bf16(*args)
+    assert rc == mm.MMRELU_OK, mm.status_string(rc)
+    torch.cuda.synchronize()
+    whole = to_host(fc)
+    c = whole[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+    r = oracle.mmrelu(a, b)
+    if dtype == "f32":
+        np.testing.assert_array_equal(c[:, :N].astype(np.float64), r)
+        pad = np.concatenate([c[:, N:].ravel(), whole[:offs[2]], whole[offs[2] + M * ldc:]])
+        assert np.all(np.isnan(pad)), "wrote outside C"
+    else:
+        np.testing.assert_array_equal(c[:, :N], bf16_round_ref(r))
+        pad = np.concatenate([c[:, N:].ravel(), whole[:offs[2]], whole[offs[2] + M * ldc:]])
+        assert np.all(np.isnan(datagen.bf16_bits_to_f32(pad))), "wrote outside C"
